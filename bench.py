@@ -1,0 +1,244 @@
+"""Benchmark of the fused LongFlow decode step (attention + LongFlowScore +
+eviction) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3_8b]
+
+A step is one call of the operator: the KV-slot write of the previous choice,
+attention over the static cache with its mask, the per-slot scores and the
+next evicted slot for every (sequence, KV head), all in one kernel launch.
+The default workload is the Qwen3-8B-shaped layer (batch 128, 32 query / 8
+KV heads, d 128, 3200 slots, bf16 K/V).  Inputs of every step are generated
+and uploaded before timing; the evicted slots go from step to step on the
+device.  Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused decode-attn+evict: KV GB/s (% HBM peak), steps/s at B=128, 3200 slots"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kv_05_amd", "csrc", n)
+                  for n in ("longflow_kernels.hip", "layout.h", "launch.h", "longflow_api.cpp")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def valid_slots(mask):
+    return int(np.count_nonzero(mask))
+
+
+def kv_bytes(wl, mask):
+    """Valid K and V rows read per step (bf16)."""
+    return valid_slots(mask) * wl.Hkv * wl.d * 2 * 2
+
+
+def algorithmic_bytes(wl, mask):
+    """Bytes one step must move: valid K/V, the mask, Q, the new K/V read and
+    written, O, fp32 scores of every slot, prev and evict slot indices."""
+    B, Hq, Hkv, d, S = wl.B, wl.Hq, wl.Hkv, wl.d, wl.S
+    return (kv_bytes(wl, mask) + B * S + B * Hq * d * 2 + 4 * B * Hkv * d * 2 + B * Hq * d * 2
+            + B * Hkv * S * 4 + 2 * B * Hkv * 4)
+
+
+def measured_traffic(workload, nsplit):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources for this workload and split."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"{workload}/nsplit{nsplit}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, mask, max_pairs):
+    """The fp64 oracle on a bounded sample of the same workload (first step),
+    single-threaded, scaled by valid K/V bytes to the whole step."""
+    from threadpoolctl import threadpool_limits
+
+    from decode_attention_kv_05_amd import workloads as W
+    from oracle import decode_step
+
+    nb = max(1, min(wl.B, -(-max_pairs // wl.Hkv)))
+    batch = list(range(nb))
+    k, v, m = W.initial_cache(wl, batch)
+    q, nk, nv = W.step_inputs(wl, 0, batch)
+    prev = W.first_prev_slot(wl, batch)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        decode_step(q, k, v, m, nk, nv, prev, wl.scale)
+        dt = time.perf_counter() - t0
+    frac = valid_slots(m) / max(1, valid_slots(mask))
+    s_per_step = dt / frac
+    return {
+        "value": round(kv_bytes(wl, mask) / s_per_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{nb * wl.Hkv} of {wl.B * wl.Hkv} (sequence, KV head) pairs of step 0 "
+                  f"({dt:.1f} s), scaled by valid K/V bytes; numpy fp64, BLAS limited to 1 thread",
+        "steps_per_s": round(1.0 / s_per_step, 6),
+        "s_per_step": round(s_per_step, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--nsplit", type=int, default=None, help="slot splits per pair (default: library plan)")
+    ap.add_argument("--cpu-pairs", type=int, default=384, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator shards by sequence or KV head with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_kv_05_amd.build import ensure_built
+    ensure_built()
+    from decode_attention_kv_05_amd import longflow as lf
+    from decode_attention_kv_05_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("no HIP device visible")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    wl = W.WORKLOADS[args.workload]
+    K, Wm = args.steps, args.warmup
+    log(f"device {props.name} ({props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB); "
+        f"workload {wl}")
+
+    t0 = time.time()
+    k, v, mask = W.initial_cache(wl)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    dk, dv = to_dev(k), to_dev(v)
+    del k, v
+    dm = torch.from_numpy(mask).to(dev)
+    n_inputs = max(1, min(wl.steps, K + Wm))
+    qs, nks, nvs = [], [], []
+    for t in range(n_inputs):
+        q, nk, nv = W.step_inputs(wl, t)
+        qs.append(to_dev(q))
+        nks.append(to_dev(nk))
+        nvs.append(to_dev(nv))
+    log(f"inputs generated and resident in HBM in {time.time() - t0:.1f} s ({n_inputs} distinct steps)")
+
+    nsplit = args.nsplit or lf.plan_nsplit(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S)
+    ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, nsplit, dev)
+    out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
+    scores = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device=dev)
+    slots = [torch.full((wl.B, wl.Hkv), -1, dtype=torch.int32, device=dev),
+             torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        i = t % n_inputs
+        lf.longflow_decode(qs[i], dk, dv, dm, nks[i], nvs[i], slots[t % 2], scale=float(wl.scale),
+                           out=out, scores=scores, evict_slot=slots[(t + 1) % 2], workspace=ws,
+                           nsplit=nsplit, stream=stream)
+
+    for t in range(Wm):
+        step(t)
+    torch.cuda.synchronize(dev)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    for t in range(K):
+        starts[t].record(stream)
+        step(Wm + t)
+        ends[t].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    total_ms = starts[0].elapsed_time(ends[-1])
+    per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = total_ms / K
+    status = lf.lf_read_device_status(ws)
+    if status:
+        raise RuntimeError(f"device status flags set during the run: {status:#x}")
+
+    kvb = kv_bytes(wl, mask)
+    algb = algorithmic_bytes(wl, mask)
+    launch_s = float(per_launch.mean()) / 1e3
+    achieved = algb / launch_s / 1e9
+    traffic = measured_traffic(wl.name, nsplit)
+    result = {
+        "metric": METRIC,
+        "value": round(kvb / (ms_per_step / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+            "head_dim": wl.d, "slots": wl.S, "valid_slots": valid_slots(mask), "nsplit": nsplit,
+            "kv_dtype": "bf16", "accumulate": "f32",
+        },
+        "steps_per_s": round(1e3 / ms_per_step, 2),
+        "kv_GBps": round(kvb / (ms_per_step / 1e3) / 1e9, 2),
+        "alg_GBps": round(algb / (ms_per_step / 1e3) / 1e9, 2),
+        "pct_hbm_peak": round(100 * algb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "alg_bytes_per_step": algb,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "longflow_decode_kernel",
+            "launch_us_mean": round(launch_s * 1e6, 2),
+            "launch_us_p50": round(float(np.median(per_launch)) * 1e3, 2),
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        result["cpu_baseline"] = cpu_baseline(wl, mask, args.cpu_pairs)
+        log(f"cpu baseline took {time.time() - t0:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

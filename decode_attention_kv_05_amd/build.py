@@ -1,0 +1,65 @@
+"""Build liblongflow.so (the HIP kernels and their C ABI) in-tree for gfx950.
+
+    python -m decode_attention_kv_05_amd.build
+
+The library is written next to this file so it travels with the source tree.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "liblongflow.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = [os.path.join(CSRC, "longflow_api.cpp"), os.path.join(CSRC, "longflow_kernels.hip")]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def compile_command(out_path):
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # keep the compiler from forming packed fp32 vector ops
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", out_path,
+    ]
+
+
+def build(verbose=False):
+    """Compile the library (always) and return its path."""
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = compile_command(tmp)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+    if verbose:
+        noise = "is not a recognized feature for this target"
+        msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+        if msg.strip():
+            sys.stderr.write(msg + "\n")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def ensure_built():
+    """Path of the built library, building it only if it is absent."""
+    if not os.path.exists(LIB_PATH):
+        build()
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

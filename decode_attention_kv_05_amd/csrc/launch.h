@@ -1,0 +1,35 @@
+// Kernel parameter block and launch entry points shared by the host API
+// (longflow_api.cpp) and the kernels (longflow_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lf {
+
+struct DecodeParams {
+  const uint16_t* q;      // bf16 [B][Hq][d]
+  uint16_t* k;            // bf16 [B][Hkv][S][d]
+  uint16_t* v;            // bf16 [B][Hkv][S][d]
+  const uint8_t* mask;    // [B][S]
+  const uint16_t* new_k;  // bf16 [B][Hkv][d]
+  const uint16_t* new_v;  // bf16 [B][Hkv][d]
+  const int32_t* prev;    // [B][Hkv]
+  uint16_t* out;          // bf16 [B][Hq][d]
+  float* scores;          // [B][Hkv][S]
+  int32_t* evict;         // [B][Hkv]
+  uint32_t* status;       // workspace: LF_DEV_* bits
+  uint32_t* counters;     // workspace: [B*Hkv] finished splits
+  float* part_ml;         // workspace: [pairs][nsplit][GP][2]
+  float* part_o;          // workspace: [pairs][nsplit][GP][d]
+  float* ws_logit;        // workspace: [pairs][S][GP]
+  float* ws_vnorm;        // workspace: [pairs][S]
+  int Hq, Hkv, G, S, nsplit, split_len;
+  float qscale;           // logit scale times log2(e)
+};
+
+hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nblocks, size_t lds,
+                         hipStream_t stream);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
+
+}  // namespace lf

@@ -1,0 +1,261 @@
+// Host side of liblongflow.so: argument checks, split planning, workspace
+// layout and the stream-ordered launch.  Declarations and the operator's
+// definition are in include/longflow.h.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+#include "layout.h"
+#include "longflow.h"
+
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int max_split_len(int gp) { return (int)(lf::kLogitLdsBudget / ((size_t)gp * 4)); }
+
+}  // namespace
+
+extern "C" {
+
+int lf_version(void) { return LF_ABI_VERSION; }
+
+const char* lf_strerror(int code) {
+  switch (code) {
+    case LF_OK: return "ok";
+    case LF_E_NULL: return "a required pointer is NULL";
+    case LF_E_SHAPE: return "unsupported or inconsistent sizes";
+    case LF_E_ALIGN: return "a pointer misses its required alignment";
+    case LF_E_ALIAS: return "an output overlaps an input or another output";
+    case LF_E_WORKSPACE: return "workspace too small";
+    case LF_E_HIP: return "HIP runtime call or kernel launch failed";
+    case LF_E_NSPLIT: return "slot split count not usable for this shape";
+    case LF_E_VALUE: return "non-finite scale";
+    default: return "unknown longflow status code";
+  }
+}
+
+int lf_check_shape(int B, int Hq, int Hkv, int d, int S) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || S < 1) return LF_E_SHAPE;
+  if (d != 64 && d != 128) return LF_E_SHAPE;
+  if (Hq % Hkv != 0) return LF_E_SHAPE;
+  if (Hq / Hkv > lf::kMaxGroup) return LF_E_SHAPE;
+  if ((int64_t)B * Hkv > INT_MAX || (int64_t)B * Hq > INT_MAX) return LF_E_SHAPE;
+  return LF_OK;
+}
+
+int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nsplit) {
+  if (!nsplit) return LF_E_NULL;
+  int rc = lf_check_shape(B, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  if (num_cus < 1) num_cus = 1;
+  const int gp = lf::padded_group(Hq / Hkv);
+  const int64_t pairs = (int64_t)B * Hkv > 0 ? (int64_t)B * Hkv : 1;
+  // The logits of a split must fit the LDS budget.
+  const int64_t need = ((int64_t)S + max_split_len(gp) - 1) / max_split_len(gp);
+  // Aim for about four workgroups per compute unit, but do not cut splits
+  // below 256 slots just to get there.
+  const int64_t target = (4LL * num_cus + pairs - 1) / pairs;
+  int64_t n = target;
+  const int64_t cap = ((int64_t)S + 255) / 256;
+  if (n > cap) n = cap;
+  if (n < need) n = need;
+  if (n < 1) n = 1;
+  if (n > lf::kMaxSplits) return LF_E_SHAPE;
+  int len, eff;
+  lf::split_geometry(S, (int)n, &len, &eff);
+  *nsplit = eff;
+  return LF_OK;
+}
+
+int lf_workspace_size(int B, int Hq, int Hkv, int d, int S, int nsplit, size_t* bytes) {
+  if (!bytes) return LF_E_NULL;
+  int rc = lf_check_shape(B, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  if (nsplit < 1 || nsplit > S || nsplit > lf::kMaxSplits) return LF_E_NSPLIT;
+  int len, eff;
+  lf::split_geometry(S, nsplit, &len, &eff);
+  *bytes = lf::workspace_layout(B, Hkv, d, S, lf::padded_group(Hq / Hkv), eff).total;
+  return LF_OK;
+}
+
+int lf_device_num_cus(int* num_cus) {
+  if (!num_cus) return LF_E_NULL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LF_E_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *num_cus = cached;
+      return LF_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return LF_E_HIP;
+  if (dev >= 0 && dev < kMaxDevices) g_num_cus[dev].store(n, std::memory_order_relaxed);
+  *num_cus = n;
+  return LF_OK;
+}
+
+int lf_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return LF_E_NULL;
+  if (misaligned(workspace, 256)) return LF_E_ALIGN;
+  if (workspace_bytes < 256 || workspace_bytes % 4 != 0) return LF_E_WORKSPACE;
+  return lf::launch_fill_u32(static_cast<uint32_t*>(workspace), workspace_bytes / 4, 0u,
+                             static_cast<hipStream_t>(stream)) == hipSuccess
+             ? LF_OK
+             : LF_E_HIP;
+}
+
+int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                const void* k_cache, const void* v_cache, const uint8_t* mask, const void* new_k,
+                const void* new_v, const int32_t* prev_slot, const void* out, const float* scores,
+                const int32_t* evict_slot, const void* workspace, size_t workspace_bytes,
+                int nsplit) {
+  int rc = lf_check_shape(B, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  if (!std::isfinite(scale)) return LF_E_VALUE;
+  if (B == 0) return LF_OK;
+  if (!q || !k_cache || !v_cache || !mask || !new_k || !new_v || !prev_slot || !out || !scores ||
+      !evict_slot || !workspace)
+    return LF_E_NULL;
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) ||
+      misaligned(new_k, 16) || misaligned(new_v, 16) || misaligned(out, 16) ||
+      misaligned(scores, 4) || misaligned(prev_slot, 4) || misaligned(evict_slot, 4) ||
+      misaligned(workspace, 256))
+    return LF_E_ALIGN;
+  if (nsplit < 1 || nsplit > S || nsplit > lf::kMaxSplits) return LF_E_NSPLIT;
+  const int gp = lf::padded_group(Hq / Hkv);
+  int len, eff;
+  lf::split_geometry(S, nsplit, &len, &eff);
+  if (len > max_split_len(gp)) return LF_E_NSPLIT;
+  if ((int64_t)B * Hkv * eff > INT_MAX) return LF_E_NSPLIT;
+
+  const size_t pairs = (size_t)B * Hkv;
+  const size_t q_bytes = (size_t)B * Hq * d * 2;
+  const size_t cache_bytes = pairs * S * d * 2;
+  const size_t mask_bytes = (size_t)B * S;
+  const size_t row_bytes = pairs * d * 2;
+  const size_t idx_bytes = pairs * 4;
+  const size_t score_bytes = pairs * S * 4;
+  const size_t ws_need = lf::workspace_layout(B, Hkv, d, S, gp, eff).total;
+
+  struct Buf {
+    const void* p;
+    size_t n;
+    bool written;
+  };
+  const Buf bufs[] = {
+      {q, q_bytes, false},           {mask, mask_bytes, false},   {new_k, row_bytes, false},
+      {new_v, row_bytes, false},     {prev_slot, idx_bytes, false}, {k_cache, cache_bytes, true},
+      {v_cache, cache_bytes, true},  {out, q_bytes, true},        {scores, score_bytes, true},
+      {evict_slot, idx_bytes, true}, {workspace, ws_need, true},
+  };
+  const int nb = (int)(sizeof(bufs) / sizeof(bufs[0]));
+  for (int i = 0; i < nb; ++i)
+    for (int k = i + 1; k < nb; ++k)
+      if ((bufs[i].written || bufs[k].written) &&
+          overlaps(bufs[i].p, bufs[i].n, bufs[k].p, bufs[k].n))
+        return LF_E_ALIAS;
+  if (workspace_bytes < ws_need) return LF_E_WORKSPACE;
+  return LF_OK;
+}
+
+int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                           void* k_cache, void* v_cache, const uint8_t* mask, const void* new_k,
+                           const void* new_v, const int32_t* prev_slot, void* out, float* scores,
+                           int32_t* evict_slot, void* workspace, size_t workspace_bytes,
+                           int nsplit, void* stream) {
+  int rc = lf_validate(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v,
+                       prev_slot, out, scores, evict_slot, workspace, workspace_bytes, nsplit);
+  if (rc != LF_OK) return rc;
+  if (B == 0) return LF_OK;
+
+  const int G = Hq / Hkv;
+  const int gp = lf::padded_group(G);
+  int len, eff;
+  lf::split_geometry(S, nsplit, &len, &eff);
+  const lf::WorkspaceLayout wl = lf::workspace_layout(B, Hkv, d, S, gp, eff);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+
+  lf::DecodeParams prm{};
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.k = static_cast<uint16_t*>(k_cache);
+  prm.v = static_cast<uint16_t*>(v_cache);
+  prm.mask = mask;
+  prm.new_k = static_cast<const uint16_t*>(new_k);
+  prm.new_v = static_cast<const uint16_t*>(new_v);
+  prm.prev = prev_slot;
+  prm.out = static_cast<uint16_t*>(out);
+  prm.scores = scores;
+  prm.evict = evict_slot;
+  prm.status = reinterpret_cast<uint32_t*>(ws + wl.status);
+  prm.counters = reinterpret_cast<uint32_t*>(ws + wl.counters);
+  prm.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
+  prm.part_o = reinterpret_cast<float*>(ws + wl.part_o);
+  prm.ws_logit = reinterpret_cast<float*>(ws + wl.logit);
+  prm.ws_vnorm = reinterpret_cast<float*>(ws + wl.vnorm);
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.G = G;
+  prm.S = S;
+  prm.nsplit = eff;
+  prm.split_len = len;
+  // Logits are kept in the log2 domain: exp(scale * x) = exp2(scale * log2(e) * x).
+  prm.qscale = scale * 1.4426950408889634f;
+
+  const int nblocks = B * Hkv * eff;
+  const size_t lds = lf::lds_layout(d, gp, len).total;
+  return lf::launch_decode(prm, d, gp, nblocks, lds, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? LF_OK
+             : LF_E_HIP;
+}
+
+int longflow_decode(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                    void* k_cache, void* v_cache, const uint8_t* mask, const void* new_k,
+                    const void* new_v, const int32_t* prev_slot, void* out, float* scores,
+                    int32_t* evict_slot, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = lf_check_shape(B, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  if (B == 0) return std::isfinite(scale) ? LF_OK : LF_E_VALUE;
+  int cus = 0;
+  rc = lf_device_num_cus(&cus);
+  if (rc != LF_OK) return rc;
+  int nsplit = 1;
+  rc = lf_plan_nsplit(B, Hq, Hkv, d, S, cus, &nsplit);
+  if (rc != LF_OK) return rc;
+  return longflow_decode_nsplit(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v,
+                                prev_slot, out, scores, evict_slot, workspace, workspace_bytes,
+                                nsplit, stream);
+}
+
+int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags) {
+  if (!workspace || !flags) return LF_E_NULL;
+  if (misaligned(workspace, 256)) return LF_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return LF_E_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LF_E_HIP;
+  *flags = v;
+  return LF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+"""ctypes binding of liblongflow.so (see include/longflow.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype,
+shape and contiguity and handed over as raw pointers together with torch's
+current HIP stream.  Every step of the decode runs in the library's HIP
+kernels.  Importing this module fails if the library has not been built.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+LF_OK = 0
+LF_E_NULL = -1
+LF_E_SHAPE = -2
+LF_E_ALIGN = -3
+LF_E_ALIAS = -4
+LF_E_WORKSPACE = -5
+LF_E_HIP = -6
+LF_E_NSPLIT = -7
+LF_E_VALUE = -8
+
+LF_DEV_BAD_PREV = 0x1
+LF_DEV_WRITE_MASKED = 0x2
+
+EXPORTED = (
+    "lf_version", "lf_strerror", "lf_check_shape", "lf_plan_nsplit", "lf_workspace_size",
+    "lf_device_num_cus", "lf_workspace_init", "lf_validate", "longflow_decode",
+    "longflow_decode_nsplit", "lf_read_device_status",
+)
+
+_i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m decode_attention_kv_05_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "lf_version": ([], _i),
+        "lf_strerror": ([_i], ctypes.c_char_p),
+        "lf_check_shape": ([_i] * 5, _i),
+        "lf_plan_nsplit": ([_i] * 6 + [ctypes.POINTER(_i)], _i),
+        "lf_workspace_size": ([_i] * 6 + [ctypes.POINTER(_sz)], _i),
+        "lf_device_num_cus": ([ctypes.POINTER(_i)], _i),
+        "lf_workspace_init": ([_p, _sz, _p], _i),
+        "lf_validate": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i], _i),
+        "longflow_decode": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _p], _i),
+        "longflow_decode_nsplit": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i, _p], _i),
+        "lf_read_device_status": ([_p, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+class LongflowError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {lf_strerror(code)} (code {code})")
+
+
+def _check(rc, where):
+    if rc != LF_OK:
+        if rc in (LF_E_SHAPE, LF_E_ALIGN, LF_E_ALIAS, LF_E_NULL, LF_E_NSPLIT, LF_E_VALUE, LF_E_WORKSPACE):
+            raise ValueError(f"{where}: {lf_strerror(rc)} (code {rc})")
+        raise LongflowError(rc, where)
+
+
+def lf_version():
+    return _lib.lf_version()
+
+
+def lf_strerror(code):
+    return _lib.lf_strerror(code).decode()
+
+
+def lf_check_shape(B, Hq, Hkv, d, S):
+    return _lib.lf_check_shape(B, Hq, Hkv, d, S)
+
+
+def lf_plan_nsplit(B, Hq, Hkv, d, S, num_cus):
+    out = _i(0)
+    _check(_lib.lf_plan_nsplit(B, Hq, Hkv, d, S, num_cus, ctypes.byref(out)), "lf_plan_nsplit")
+    return out.value
+
+
+def lf_workspace_size(B, Hq, Hkv, d, S, nsplit):
+    out = _sz(0)
+    _check(_lib.lf_workspace_size(B, Hq, Hkv, d, S, nsplit, ctypes.byref(out)), "lf_workspace_size")
+    return out.value
+
+
+def lf_device_num_cus():
+    out = _i(0)
+    _check(_lib.lf_device_num_cus(ctypes.byref(out)), "lf_device_num_cus")
+    return out.value
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def lf_workspace_init(workspace, stream=None):
+    _check(_lib.lf_workspace_init(ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                                  _stream_ptr(stream, workspace.device)), "lf_workspace_init")
+
+
+def lf_validate(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v, prev_slot,
+                out, scores, evict_slot, workspace, workspace_bytes, nsplit):
+    """Host-only check on raw addresses (ints); returns the lf_status code."""
+    ptrs = [ctypes.c_void_p(x) for x in (q, k_cache, v_cache, mask, new_k, new_v, prev_slot,
+                                          out, scores, evict_slot, workspace)]
+    return _lib.lf_validate(B, Hq, Hkv, d, S, float(scale), *ptrs, workspace_bytes, nsplit)
+
+
+def plan_nsplit(B, Hq, Hkv, d, S):
+    """Split count the library picks on the current device."""
+    return lf_plan_nsplit(B, Hq, Hkv, d, S, lf_device_num_cus())
+
+
+def new_workspace(B, Hq, Hkv, d, S, nsplit=None, device=None):
+    """Zeroed device workspace sized for (shape, nsplit); nsplit None = the device plan."""
+    if nsplit is None:
+        nsplit = plan_nsplit(B, Hq, Hkv, d, S)
+    n = lf_workspace_size(B, Hq, Hkv, d, S, nsplit)
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
+                    out=None, scores=None, evict_slot=None, workspace=None, nsplit=None,
+                    stream=None):
+    """One fused decode step; returns (out, scores, evict_slot).
+
+    q [B, Hq, d] bf16; k_cache, v_cache [B, Hkv, S, d] bf16 (updated in place);
+    mask [B, S] uint8 or bool; new_k, new_v [B, Hkv, d] bf16; prev_slot
+    [B, Hkv] int32.  Outputs are allocated when not given: out [B, Hq, d]
+    bf16, scores [B, Hkv, S] float32, evict_slot [B, Hkv] int32.  scale
+    defaults to 1/sqrt(d).  nsplit None uses the library's plan for the
+    device.  The work is enqueued on `stream` (default: torch's current
+    stream) and not waited for.
+    """
+    B, Hq, d = q.shape
+    Hkv, S = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, Hq, d), dev)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, S, d), dev)
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, S, d), dev)
+    _need(mask, "mask", (torch.uint8, torch.bool), (B, S), dev)
+    _need(new_k, "new_k", torch.bfloat16, (B, Hkv, d), dev)
+    _need(new_v, "new_v", torch.bfloat16, (B, Hkv, d), dev)
+    _need(prev_slot, "prev_slot", torch.int32, (B, Hkv), dev)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if nsplit is None:
+        nsplit = plan_nsplit(B, Hq, Hkv, d, S) if B > 0 else 1
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    if scores is None:
+        scores = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+    if evict_slot is None:
+        evict_slot = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    _need(out, "out", torch.bfloat16, (B, Hq, d), dev)
+    _need(scores, "scores", torch.float32, (B, Hkv, S), dev)
+    _need(evict_slot, "evict_slot", torch.int32, (B, Hkv), dev)
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, d, S, nsplit, dev) if B > 0 else torch.zeros(256, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = _lib.longflow_decode_nsplit(
+        B, Hq, Hkv, d, S, float(scale), ptr(q), ptr(k_cache), ptr(v_cache), ptr(mask),
+        ptr(new_k), ptr(new_v), ptr(prev_slot), ptr(out), ptr(scores), ptr(evict_slot),
+        ptr(workspace), workspace.numel() * workspace.element_size(), int(nsplit),
+        _stream_ptr(stream, dev))
+    _check(rc, "longflow_decode")
+    return out, scores, evict_slot
+
+
+def lf_read_device_status(workspace, stream=None):
+    """LF_DEV_* bits recorded in the workspace (synchronises the stream)."""
+    flags = ctypes.c_uint32(0)
+    _check(_lib.lf_read_device_status(ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream, workspace.device),
+                                      ctypes.byref(flags)), "lf_read_device_status")
+    return flags.value

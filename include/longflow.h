@@ -1,0 +1,157 @@
+/*
+ * longflow.h -- C ABI of liblongflow.so, LongFlow's fused decode operator for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source: "LongFlow: Efficient KV Cache Compression for Reasoning Models"
+ * (arXiv 2603.11504).  The abstract describes one operator that fuses
+ * attention, importance estimation and token eviction; the Figure 2 caption
+ * gives its data flow:
+ *   Left   the current token's K/V overwrite the slot chosen at the previous
+ *          step; the static KV cache, the mask and the query then yield the
+ *          attention output and the slot to overwrite at the next step;
+ *   Middle K/V and mask are streamed from HBM into on-chip memory by block;
+ *   Right  the product of P and V is split in two steps, an intermediate G and
+ *          then O, and the importance score (LongFlowScore) comes from G.
+ *
+ * What the operator computes (the pages leave the exact form of G and of the
+ * score open; this library fixes it as follows):
+ *   for every sequence b and KV head j, with G = Hq / Hkv query heads
+ *   h = j*G .. j*G+G-1 sharing KV head j and V_b = { i : mask[b][i] != 0 }:
+ *     1. if prev_slot[b][j] != -1:  K[b][j][prev] = new_k[b][j],
+ *                                   V[b][j][prev] = new_v[b][j]
+ *     2. s[h][i] = scale * <q[b][h], K[b][j][i]>           for i in V_b
+ *     3. p[h][i] = softmax over V_b of s[h][.]
+ *     4. G[h][i] = p[h][i] * V[b][j][i]     (never materialised: the L1 norm
+ *                                             of p*v is p * |v|_1 since p >= 0)
+ *     5. out[b][h] = sum_i G[h][i]
+ *     6. scores[b][j][i] = sum_h |G[h][i]|_1 for i in V_b, +inf otherwise
+ *     7. evict_slot[b][j] = lowest i in V_b with minimum score; -1 if V_b is
+ *        empty (then out = 0 and every score is +inf)
+ *   The slot written in step 1 is part of the same step's attention.
+ *
+ * Data types and layouts (all row-major, contiguous, device memory):
+ *   bf16 tensors are passed as raw 16-bit patterns (uint16_t / void*).
+ *   q          bf16  [B][Hq][d]
+ *   k_cache    bf16  [B][Hkv][S][d]   read, one row per (b, j) overwritten
+ *   v_cache    bf16  [B][Hkv][S][d]   read, one row per (b, j) overwritten
+ *   mask       uint8 [B][S]           nonzero = valid slot; shared by the KV heads
+ *   new_k      bf16  [B][Hkv][d]
+ *   new_v      bf16  [B][Hkv][d]
+ *   prev_slot  int32 [B][Hkv]         -1 = nothing to write
+ *   out        bf16  [B][Hq][d]       written (fp32 accumulate, round to nearest even)
+ *   scores     fp32  [B][Hkv][S]      written
+ *   evict_slot int32 [B][Hkv]         written
+ * Supported shapes: B >= 0 (B = 0 is a no-op), Hq >= 1, Hkv >= 1,
+ * Hq % Hkv == 0, 1 <= Hq / Hkv <= 8, d in {64, 128}, S >= 1.
+ * Alignment: q, k_cache, v_cache, new_k, new_v, out on 16 bytes; scores,
+ * prev_slot, evict_slot on 4 bytes; workspace on 256 bytes.
+ *
+ * Ownership and concurrency: the caller owns every buffer; the library keeps
+ * no pointer after a call returns and holds no global state besides a cached
+ * per-device compute-unit count.  Compute calls are asynchronous: they
+ * enqueue work on `stream` (a hipStream_t; NULL = the default stream) and
+ * return; results are valid once the stream has reached that point.  No call
+ * synchronises, allocates device memory or copies to the host except
+ * lf_read_device_status.  Two calls that share a workspace must be ordered on
+ * one stream.
+ *
+ * Errors: every entry point returns LF_OK (0) or a negative lf_status code
+ * from host-side checks made before anything is enqueued; nothing is enqueued
+ * on error.  Conditions that depend on device-resident values (prev_slot)
+ * cannot be checked on the host without a synchronisation: they are recorded
+ * as LF_DEV_* bits in a status word inside the workspace (see
+ * lf_read_device_status).  NaN or Inf in valid slots propagate unchecked;
+ * the contents of masked slots are never read.
+ */
+#ifndef LONGFLOW_H
+#define LONGFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LF_ABI_VERSION 1
+
+typedef enum lf_status {
+  LF_OK = 0,
+  LF_E_NULL = -1,       /* a required pointer is NULL                          */
+  LF_E_SHAPE = -2,      /* unsupported or inconsistent sizes                   */
+  LF_E_ALIGN = -3,      /* a pointer misses its required alignment             */
+  LF_E_ALIAS = -4,      /* an output overlaps an input or another output       */
+  LF_E_WORKSPACE = -5,  /* workspace too small                                 */
+  LF_E_HIP = -6,        /* a HIP runtime call or kernel launch failed          */
+  LF_E_NSPLIT = -7,     /* requested slot split count not usable for the shape */
+  LF_E_VALUE = -8       /* non-finite scale                                    */
+} lf_status;
+
+/* Device status bits, accumulated in the workspace across calls until cleared. */
+#define LF_DEV_BAD_PREV 0x1u     /* prev_slot outside {-1} U [0, S): write skipped */
+#define LF_DEV_WRITE_MASKED 0x2u /* prev_slot named a masked slot: written, unused */
+
+/* ABI version (LF_ABI_VERSION). */
+int lf_version(void);
+
+/* Static description of an lf_status code; never NULL. */
+const char* lf_strerror(int code);
+
+/* Host-only shape check; returns LF_OK or LF_E_SHAPE.  Touches no device. */
+int lf_check_shape(int B, int Hq, int Hkv, int d, int S);
+
+/* Host-only choice of the number of slot splits per (sequence, KV head) for
+ * a device with `num_cus` compute units.  Writes the count to *nsplit.  A
+ * split count of 1 keeps the whole step of a (b, j) pair in one workgroup;
+ * larger counts split the slots (flash-decoding) and combine the partial
+ * softmax statistics in the same launch. */
+int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nsplit);
+
+/* Host-only workspace size in bytes for an explicit split count (>= 1). */
+int lf_workspace_size(int B, int Hq, int Hkv, int d, int S, int nsplit, size_t* bytes);
+
+/* Compute units of the current HIP device (cached per device). */
+int lf_device_num_cus(int* num_cus);
+
+/* Zero the workspace's status word and combine counters with a fill kernel
+ * enqueued on `stream`.  Required once before the first longflow_decode on a
+ * workspace whose contents are not already zero; every completed call leaves
+ * the counters at zero again. */
+int lf_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only argument validation, exactly the checks longflow_decode_nsplit
+ * makes before enqueuing anything.  Pointers are compared, never dereferenced. */
+int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale,
+                const void* q, const void* k_cache, const void* v_cache,
+                const uint8_t* mask, const void* new_k, const void* new_v,
+                const int32_t* prev_slot, const void* out, const float* scores,
+                const int32_t* evict_slot, const void* workspace,
+                size_t workspace_bytes, int nsplit);
+
+/* One fused decode step (Figure 2, Left panel: write the previous choice,
+ * attend, score, choose the next slot), with the split count chosen by
+ * lf_plan_nsplit for the current device.  The workspace must hold at least
+ * lf_workspace_size(..., nsplit, ...) bytes for that count. */
+int longflow_decode(int B, int Hq, int Hkv, int d, int S, float scale,
+                    const void* q, void* k_cache, void* v_cache,
+                    const uint8_t* mask, const void* new_k, const void* new_v,
+                    const int32_t* prev_slot, void* out, float* scores,
+                    int32_t* evict_slot, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* The same step with an explicit split count (1 <= nsplit <= S). */
+int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale,
+                           const void* q, void* k_cache, void* v_cache,
+                           const uint8_t* mask, const void* new_k, const void* new_v,
+                           const int32_t* prev_slot, void* out, float* scores,
+                           int32_t* evict_slot, void* workspace, size_t workspace_bytes,
+                           int nsplit, void* stream);
+
+/* Copy the workspace's LF_DEV_* bits to *flags.  Synchronises `stream`. */
+int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LONGFLOW_H */

@@ -1,0 +1,48 @@
+"""The five named workloads at full size, in the launch configuration the
+benchmark times (the library's own split plan), for every decode step.
+
+The oracle checks a sample of (sequence, KV head) pairs in lockstep; every
+pair of every step is checked for the properties that hold at any size
+(masked scores +inf, the evicted slot is valid, holds the minimum score and
+is the lowest index among exact ties)."""
+
+import pytest
+import torch
+
+from decode_attention_kv_05_amd import workloads as W
+from gpu_util import Lockstep, Timer, global_properties, log
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    yield
+
+
+def sample_pairs(wl):
+    B, H = wl.B, wl.Hkv
+    pairs = {(0, 0), (B - 1, H - 1), (B // 2, H // 2), (B // 3, H - 2), (min(1, B - 1), 1)}
+    if wl.kind == "ragged":
+        lens = [W.valid_length(wl, b) for b in range(B)]
+        pairs |= {(lens.index(min(lens)), 0), (lens.index(max(lens)), H - 1)}
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b", "llama8b_budget", "long_reasoning", "ragged"])
+def test_full_workload(name):
+    wl = W.WORKLOADS[name]
+    pairs = sample_pairs(wl)
+    log(f"{name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} d={wl.d} S={wl.S} steps={wl.steps} pairs={pairs}")
+    with Timer("generate + upload"):
+        ls = Lockstep(wl, pairs=pairs)
+    with Timer(f"{wl.steps} lockstep steps"):
+        for t in range(wl.steps):
+            out, sc, ev = ls.step()
+            global_properties(sc, ev, ls.dm)
+            if t % 64 == 0:
+                log(f"  step {t} ok")
+    ls.check_full_cache()
+    log(f"  evictions exactly equal to the oracle's: {ls.exact}/{ls.total}")

@@ -1,0 +1,201 @@
+"""HIP operator against the fp64 oracle on the same seeded inputs.
+
+Small cases compare every (sequence, KV head) of every step (lockstep: both
+sides continue from the GPU's accepted eviction).  Acceptance: O within
+1e-2 + 1e-2 |O_ref| per element, valid scores within 1e-3 relative, masked
+scores +inf, evict slot exact except at near-ties (two smallest oracle
+scores within 1e-4 relative), cache rows bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_05_amd import workloads as W
+from gpu_util import Lockstep, bf16_dev, bf16_host, bf16_value, global_properties, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from decode_attention_kv_05_amd import longflow  # noqa: F401  (fails loudly if not built)
+    yield
+
+
+@pytest.mark.parametrize("nsplit", [None, 1, 2, 3, 7])
+def test_tiny_workload_lockstep(nsplit):
+    wl = W.WORKLOADS["tiny"]
+    log(f"tiny lockstep nsplit={nsplit}")
+    ls = Lockstep(wl, nsplit=nsplit)
+    for _ in range(wl.steps):
+        ls.step()
+    ls.check_full_cache()
+
+
+@pytest.mark.parametrize("nsplit", [1, 4])
+def test_tiny_d128(nsplit):
+    """d = 128 makes the scale 1/sqrt(128), not a power of two."""
+    wl = W.WORKLOADS["tiny"].replace(name="tiny_d128", d=128)
+    log(f"tiny d128 nsplit={nsplit}")
+    ls = Lockstep(wl, nsplit=nsplit)
+    for _ in range(wl.steps):
+        ls.step()
+    ls.check_full_cache()
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nsplit", [1, 3])
+def test_group_sizes_ragged_tail(G, d, nsplit):
+    """GQA groups 1..8 (3 and 5 padded to 4 and 8), a slot count that is not
+    a multiple of any tile, and ragged per-sequence valid lengths."""
+    wl = W.Workload(f"g{G}_d{d}", B=3, Hq=2 * G, Hkv=2, d=d, S=333, steps=4, kind="ragged",
+                    seed=7000 + G, len_lo=40)
+    log(f"group G={G} d={d} nsplit={nsplit}")
+    ls = Lockstep(wl, nsplit=nsplit)
+    for _ in range(wl.steps):
+        ls.step()
+    ls.check_full_cache()
+
+
+@pytest.mark.parametrize("kind", ["plain", "sinks", "lognormal_v", "ragged"])
+def test_mid_size_all_pairs(kind):
+    """Real head counts and d = 128 with the oracle on every pair."""
+    S = {"plain": 3200, "sinks": 2400, "lognormal_v": 4096, "ragged": 2048}[kind]
+    Hq = 64 if kind == "lognormal_v" else 32
+    wl = W.Workload(f"mid_{kind}", B=2, Hq=Hq, Hkv=8, d=128, S=S, steps=3, kind=kind, seed=8100)
+    log(f"mid-size {kind}")
+    ls = Lockstep(wl)
+    for _ in range(wl.steps):
+        ls.step()
+    ls.check_full_cache()
+
+
+def _empty_row_case(nsplit):
+    wl = W.Workload("edge", B=3, Hq=4, Hkv=2, d=128, S=100, steps=1, seed=42)
+    k, v, mask = W.initial_cache(wl)
+    mask[1, :] = 0           # sequence 1: no valid slot
+    mask[2, :] = 0
+    mask[2, 57] = 1          # sequence 2: one valid slot
+    for b in (1, 2):
+        k[b][:, mask[b] == 0] = W.BF16_NAN
+        v[b][:, mask[b] == 0] = W.BF16_NAN
+    return wl, (k, v, mask)
+
+
+@pytest.mark.parametrize("nsplit", [1, 3])
+def test_empty_and_single_slot_rows(nsplit):
+    wl, state = _empty_row_case(nsplit)
+    k, v, mask = state
+    log(f"empty/single rows nsplit={nsplit}")
+    ls = Lockstep(wl, nsplit=nsplit, state=(k.copy(), v.copy(), mask.copy()))
+    out, sc, ev = ls.step()
+    ev = ev.cpu().numpy()
+    assert np.all(ev[1] == -1) and np.all(ev[2] == 57)
+    o = bf16_value(bf16_host(out))
+    assert np.all(o[1] == 0)
+    assert np.all(np.isposinf(sc[1].cpu().numpy()))
+    for j in range(2):
+        vv = bf16_value(v[2, j, 57])
+        assert np.array_equal(o[2, 2 * j], vv) and np.array_equal(o[2, 2 * j + 1], vv)
+
+
+@pytest.mark.parametrize("nsplit", [1, 4])
+def test_prev_slot_status_flags(nsplit):
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("flags", B=2, Hq=8, Hkv=2, d=64, S=64, steps=1, seed=43, valid=48)
+    k, v, mask = W.initial_cache(wl)
+    q, nk, nv = W.step_inputs(wl, 0)
+    dk, dv = bf16_dev(k), bf16_dev(v)
+    ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, nsplit)
+    log(f"status flags nsplit={nsplit}")
+    # out of range: no write anywhere, flag set
+    prev = torch.tensor([[64, -5], [-1, -1]], dtype=torch.int32, device="cuda")
+    lf.longflow_decode(bf16_dev(q), dk, dv, torch.from_numpy(mask).cuda(), bf16_dev(nk), bf16_dev(nv), prev,
+                       workspace=ws, nsplit=nsplit)
+    assert lf.lf_read_device_status(ws) == lf.LF_DEV_BAD_PREV
+    assert np.array_equal(bf16_host(dk), k) and np.array_equal(bf16_host(dv), v)
+    # masked target: written, flagged, and invisible to the result
+    lf.lf_workspace_init(ws)
+    prev = torch.tensor([[50, -1], [-1, 3]], dtype=torch.int32, device="cuda")
+    out, sc, ev = lf.longflow_decode(bf16_dev(q), dk, dv, torch.from_numpy(mask).cuda(), bf16_dev(nk),
+                                     bf16_dev(nv), prev, workspace=ws, nsplit=nsplit)
+    assert lf.lf_read_device_status(ws) == lf.LF_DEV_WRITE_MASKED
+    assert np.array_equal(bf16_host(dk[0, 0, 50]), nk[0, 0])
+    assert np.array_equal(bf16_host(dk[1, 1, 3]), nk[1, 1])
+    assert np.isposinf(sc[0, 0, 50].item())
+    lf.lf_workspace_init(ws)
+    assert lf.lf_read_device_status(ws) == 0
+
+
+def test_empty_batch_is_a_no_op():
+    from decode_attention_kv_05_amd import longflow as lf
+    e = lambda *s, dt=torch.bfloat16: torch.empty(s, dtype=dt, device="cuda")
+    out, sc, ev = lf.longflow_decode(e(0, 8, 128), e(0, 2, 10, 128), e(0, 2, 10, 128), e(0, 10, dt=torch.uint8),
+                                     e(0, 2, 128), e(0, 2, 128), e(0, 2, dt=torch.int32))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 128) and sc.shape == (0, 2, 10) and ev.shape == (0, 2)
+
+
+@pytest.mark.parametrize("nsplit", [1, 5])
+def test_deterministic(nsplit):
+    """Same inputs twice: bitwise the same O, scores and evict (no float atomics)."""
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("det", B=4, Hq=32, Hkv=8, d=128, S=1000, steps=1, seed=44)
+    k, v, mask = W.initial_cache(wl)
+    q, nk, nv = W.step_inputs(wl, 0)
+    res = []
+    for rep in range(2):
+        dk, dv = bf16_dev(k), bf16_dev(v)
+        prev = torch.full((4, 8), 7, dtype=torch.int32, device="cuda")
+        out, sc, ev = lf.longflow_decode(bf16_dev(q), dk, dv, torch.from_numpy(mask).cuda(), bf16_dev(nk),
+                                         bf16_dev(nv), prev, nsplit=nsplit)
+        torch.cuda.synchronize()
+        res.append((bf16_host(out), sc.cpu().numpy(), ev.cpu().numpy()))
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_checkpoint_resume_is_bitwise():
+    """Decode state is (K, V, mask, prev_slot): 16 straight steps equal 8 steps,
+    a host round trip of that state, and 8 more."""
+    wl = W.Workload("ckpt", B=2, Hq=8, Hkv=2, d=128, S=500, steps=16, seed=45)
+    a = Lockstep(wl)
+    for _ in range(16):
+        out_a, sc_a, ev_a = a.step(check=False)
+    b = Lockstep(wl)
+    for _ in range(8):
+        b.step(check=False)
+    saved = (bf16_host(b.dk), bf16_host(b.dv), b.dm.cpu().numpy(), b.dprev.cpu().numpy())
+    c = Lockstep(wl, state=(saved[0], saved[1], saved[2]))
+    c.prev = saved[3]
+    c.dprev = torch.from_numpy(saved[3]).cuda()
+    c.t = 8
+    for _ in range(8):
+        out_c, sc_c, ev_c = c.step(check=False)
+    assert torch.equal(out_a.view(torch.int16), out_c.view(torch.int16))
+    assert torch.equal(sc_a, sc_c) and torch.equal(ev_a, ev_c)
+    assert torch.equal(a.dk.view(torch.int16), c.dk.view(torch.int16))
+
+
+def test_twins_tie_to_lowest_index():
+    """Exact duplicate K/V rows get bit-identical scores; the lower slot wins."""
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("twins", B=1, Hq=4, Hkv=1, d=128, S=600, steps=1, seed=46)
+    k, v, mask = W.initial_cache(wl)
+    v[0, 0, 450] = (v[0, 0, 450].astype(np.uint32) & 0x8000 | 0x2000).astype(np.uint16)  # tiny |v|
+    k[0, 0, 120] = k[0, 0, 450]
+    v[0, 0, 120] = v[0, 0, 450]
+    q, nk, nv = W.step_inputs(wl, 0)
+    for nsplit in (1, 2, 4):
+        out, sc, ev = lf.longflow_decode(bf16_dev(q), bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda(),
+                                         bf16_dev(nk), bf16_dev(nv),
+                                         torch.full((1, 1), -1, dtype=torch.int32, device="cuda"), nsplit=nsplit)
+        torch.cuda.synchronize()
+        s = sc.cpu().numpy()
+        assert s[0, 0, 120] == s[0, 0, 450]
+        assert ev.item() == 120, (nsplit, ev.item())
+        global_properties(sc, ev, torch.from_numpy(mask).cuda())
