@@ -19,7 +19,6 @@ struct DecodeParams {
   float* scores;          // [B][Hkv][S]
   int32_t* evict;         // [B][Hkv]
   uint32_t* status;       // workspace: LF_DEV_* bits
-  uint32_t* counters;     // workspace: [B*Hkv] finished splits
   float* part_ml;         // workspace: [pairs][nsplit][GP][2]
   float* part_o;          // workspace: [pairs][nsplit][GP][d]
   float* ws_logit;        // workspace: [pairs][S][GP]

@@ -15,7 +15,18 @@
 namespace lf {
 
 constexpr int kMaxGroup = 8;          // query heads per KV head supported
-constexpr int kWaves = 4;             // wavefronts per workgroup
+// Tuning knobs of the decode kernel; the defaults are the shipped choice.
+#ifndef LF_WAVES
+#define LF_WAVES 8  // wavefronts per workgroup
+#endif
+#ifndef LF_UNROLL
+#define LF_UNROLL 8  // 16-byte row loads per lane per batch (halved for groups of 8)
+#endif
+#ifndef LF_WAVES_PER_EU
+#define LF_WAVES_PER_EU 4  // occupancy hint given to the register allocator
+#endif
+
+constexpr int kWaves = LF_WAVES;      // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64; // threads per workgroup
 constexpr int kMaxSplits = 1024;      // slot splits per (sequence, KV head)
 // LDS bytes a workgroup may spend on the logits of its slot range.
@@ -39,7 +50,6 @@ LF_HD inline void split_geometry(int S, int nsplit, int* split_len, int* nsplit_
 // Byte offsets inside the caller's workspace.
 struct WorkspaceLayout {
   size_t status;    // uint32: LF_DEV_* bits
-  size_t counters;  // uint32 [pairs]: splits finished for the current call
   size_t part_ml;   // float [pairs][nsplit][GP][2]: split max and sum of exp2
   size_t part_o;    // float [pairs][nsplit][GP][d]: split output accumulators
   size_t logit;     // float [pairs][S][GP]: log2-domain logits
@@ -52,8 +62,6 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
   const size_t pairs = (size_t)B * (size_t)Hkv;
   size_t off = 256;
   w.status = 0;
-  w.counters = off;
-  off = align_up(off + pairs * 4, 256);
   if (nsplit_eff > 1) {
     w.part_ml = off;
     off = align_up(off + pairs * nsplit_eff * gp * 2 * 4, 256);
@@ -72,22 +80,25 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
 
 // LDS layout of one workgroup, in bytes from the start of dynamic LDS.
 struct LdsLayout {
-  size_t logits;  // float [split_len][GP]; reused for the cross-wave O reduction
-  size_t mask;    // uint8 [split_len]
+  size_t logits;  // float [split_len + kRowPad][GP]; reused for the cross-wave O reduction
+  size_t mask;    // uint8 [split_len + kRowPad], zero past the split
   size_t scratch; // reductions and broadcast values
   size_t total;
 };
 
 constexpr size_t kScratchBytes = 1024;
+// Rows past the end of a split that a wave batch may touch; the mask and
+// logit arrays are padded by this much so those reads need no bounds check.
+constexpr int kRowPad = 128;
 
 LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len) {
   LdsLayout l{};
-  size_t logits = align_up((size_t)split_len * gp * 4, 16);
+  size_t logits = align_up((size_t)(split_len + kRowPad) * gp * 4, 16);
   size_t ored = (size_t)kWaves * gp * d * 4;
   l.logits = 0;
   size_t off = logits > ored ? logits : ored;
   l.mask = off;
-  off = align_up(off + split_len, 16);
+  off = align_up(off + split_len + kRowPad, 16);
   l.scratch = off;
   l.total = off + kScratchBytes;
   return l;

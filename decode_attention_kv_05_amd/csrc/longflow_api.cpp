@@ -206,7 +206,6 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
   prm.scores = scores;
   prm.evict = evict_slot;
   prm.status = reinterpret_cast<uint32_t*>(ws + wl.status);
-  prm.counters = reinterpret_cast<uint32_t*>(ws + wl.counters);
   prm.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
   prm.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   prm.ws_logit = reinterpret_cast<float*>(ws + wl.logit);

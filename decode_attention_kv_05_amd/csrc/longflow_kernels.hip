@@ -6,32 +6,36 @@
 // choice, attend, return the next slot; Middle: K/V and mask streamed from HBM
 // by block; Right: P.V split into G then O, score from G).
 //
-// One launch per decode step.  Workgroup (256 threads) = one slot range
-// ("split") of one (sequence b, KV head j) pair.
+// decode kernel: one workgroup (8 waves) per slot range ("split") of one
+// (sequence b, KV head j) pair.
 //
-//   setup    the split that owns prev_slot copies new_k/new_v into the cache
-//            row and reads that row from new_k/new_v for the rest of the step;
-//            the mask of the split is staged in LDS.
-//   phase K  K rows stream from HBM in 16-byte lane loads (a 256-byte row
-//            = 16 lanes).  Each lane dots its 8 columns with the G queries of
-//            the group; a DPP reduce-scatter across the 16 lanes leaves one
-//            head's full logit per lane group.  Logits (log2 domain: the scale
-//            is pre-multiplied by log2 e) go to LDS.
-//   softmax  block max M_h and sum L_h of exp2(s - M_h); LDS logits become
-//            e = exp2(s - M_h) in place.
-//   phase V  V rows stream the same way.  Each lane accumulates e*v for its 8
-//            columns and G heads (G = p*v is never stored: only O = sum G and
-//            |G|_1 = p*|v|_1 are needed, since p >= 0), and |v|_1 per row.
-//   finish   (single split) score_i = |v_i|_1 * sum_h e_hi / L_h is written in
-//            phase V, O = acc / L, argmin over (score bits, slot) pairs.
-//            (several splits) each split stores its (M, L, acc) partials, the
-//            logits and |v|_1; the last split of the pair to finish (atomic
-//            counter) rescales the partials to the true softmax, writes O,
-//            every score and the evicted slot, and resets the counter.
+//   setup    the split that owns prev_slot copies new_k/new_v into that cache
+//            row and reads the row from new_k/new_v for the rest of the step;
+//            the split's mask is staged in LDS.
+//   phase K  K rows stream from HBM in 16-byte lane loads (a d = 128 row is
+//            16 lanes), two batches in flight per wave.  Each lane dots its 8
+//            columns with the group's G queries; a DPP reduce-scatter over
+//            the row's lanes leaves each head's full logit in one lane group.
+//            Logits (log2 domain: the scale is pre-multiplied by log2 e) go
+//            to LDS.
+//   softmax  split max M_h and sum L_h of exp2(s - M_h); the LDS logits turn
+//            into e = exp2(s - M_h) in place.
+//   phase V  V rows stream the same way.  Each lane accumulates e * v for its
+//            8 columns and G heads, and |v|_1 per row.  G = p * v is never
+//            stored: O needs only sum_i e_i v_i / L and |G_hi|_1 = p_hi |v_i|_1
+//            because p >= 0.
+//   finish   single split: score_i = |v_i|_1 * sum_h e_hi / L_h is written in
+//            phase V, O = acc / L, and the argmin over packed (score bits,
+//            slot) words gives the evicted slot.
+//            several splits: each split writes its (M, L, acc) partials, the
+//            logits and |v|_1 to the workspace; the combine kernel launched
+//            right after on the same stream rescales them to the true
+//            softmax.  The kernel boundary orders the two, so no cross-
+//            workgroup fences are needed.
 //
-// The per-slot arithmetic is the same instruction sequence for every slot, so
-// two slots with identical K/V rows get bit-identical scores and the argmin's
-// lowest-index rule decides exact ties.
+// Every slot goes through the same instruction sequence, so two slots with
+// identical K/V rows get bit-identical scores and the lowest-index rule
+// decides exact ties.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -44,6 +48,32 @@
 namespace lf {
 
 // ------------------------------------------------------------ lane helpers
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0).  A load whose
+// offset is not below `bytes` returns zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 0);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// fp32 sum of the 8 products of two rows of 8 bf16 values, plus `acc`
+// (bf16 x bf16 products are exact in fp32).
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
 
 __device__ __forceinline__ void bf16x8_to_f32(const uint4& x, float (&f)[8]) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -69,7 +99,7 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // Value of the partner lane for step BIT of a reduction inside a 16-lane DPP
 // row.  The partner has the opposite value of lane bit BIT and the same
 // value of every higher lane bit, which is all a butterfly needs:
-//   8: row_ror:8 (lane ^ 8)        4: row_half_mirror (lane ^ 7)
+//   8: row_ror:8 (lane ^ 8)         4: row_half_mirror (lane ^ 7)
 //   2: quad_perm 2,3,0,1 (lane ^ 2) 1: quad_perm 1,0,3,2 (lane ^ 1)
 template <int BIT>
 __device__ __forceinline__ float partner(float x) {
@@ -81,9 +111,9 @@ __device__ __forceinline__ float partner(float x) {
 }
 
 // Reduce-scatter of N per-lane partial sums over the lanes of one row group.
-// While N > 1 each step keeps half of the values (upper half if the lane's
-// BIT is set) and adds the partner's copy of that half; once one value is
-// left the steps are plain butterfly adds.
+// While N > 1 each step keeps half of the values (the upper half if the
+// lane's BIT is set) and adds the partner's copy of that half; once one value
+// is left the remaining steps are plain butterfly adds.
 template <int BIT, int N>
 __device__ __forceinline__ void reduce_scatter(float* a, int c) {
   if constexpr (BIT >= 1) {
@@ -137,18 +167,71 @@ __device__ __forceinline__ uint64_t pack_candidate(float score, int slot) {
 
 constexpr uint64_t kNoCandidate = ~0ull;
 
-// ------------------------------------------------------------------ kernel
+// Keeps the scheduler from hoisting the LDS reads and conversions of later
+// rows of a batch above the current one, which would multiply the live
+// registers per wave (and so cut the waves per CU that keep loads in flight).
+#ifndef LF_ROW_FENCE_ON
+#define LF_ROW_FENCE_ON 1
+#endif
+#if LF_ROW_FENCE_ON
+#define LF_ROW_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define LF_ROW_FENCE() ((void)0)
+#endif
+
+// Ties 8 accumulators to this point of the program (an empty asm that reads
+// and writes them), so the compiler cannot gather the FMAs of all rows of a
+// batch at its end and keep every row's converted values live meanwhile.
+__device__ __forceinline__ void pin8(float (&a)[8]) {
+#if LF_ROW_FENCE_ON
+  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+               "+v"(a[6]), "+v"(a[7]));
+#endif
+}
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kInf = __builtin_huge_valf();
+
+// ------------------------------------------------------------ decode kernel
+
+template <int D, int GP>
+struct Shape {
+  static constexpr int LPR = D / 8;                     // lanes per row (16 bytes each)
+  static constexpr int RPW = 64 / LPR;                  // rows per wave load
+  static constexpr int U = GP >= 8 ? LF_UNROLL / 2 : LF_UNROLL;  // wave loads per batch
+  static constexpr int ROWS = RPW * U;                  // rows per wave batch
+  static constexpr int HPL = GP > LPR ? GP / LPR : 1;   // heads per lane after reduce-scatter
+  static constexpr int LPH = GP < LPR ? LPR / GP : 1;   // lanes holding each head
+};
+
+// One batch of U rows of a cache tensor: each lane reads its 16-byte chunk
+// of rows r0 + u * RPW + rg.  Rows past the split or masked get an offset
+// outside the buffer resource and come back as zero without a memory access;
+// bit u of the result says whether row u is valid.  Row `sub_row` takes the
+// lane's chunk of the new token (`sub`) instead of the cache contents.
+template <int D, int U, int RPW>
+__device__ __forceinline__ uint32_t load_batch(uint4 (&buf)[U], __amdgpu_buffer_rsrc_t rows,
+                                               const uint4& sub, int sub_row,
+                                               const uint8_t* mk, int r0, int rg, int c, int n) {
+  uint32_t ok = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = r0 + u * RPW + rg;
+    const bool v = mk[r] != 0;  // zero past the split
+    const uint32_t off = v ? (uint32_t)r * (D * 2) + (uint32_t)c * 16 : kOutOfRange;
+    const uint4 x = load16(rows, off);
+    buf[u] = (r == sub_row) ? sub : x;
+    ok |= (uint32_t)v << u;
+  }
+  return ok;
+}
 
 template <int D, int GP, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams p) {
-  constexpr int LPR = D / 8;                           // lanes per 16-byte-chunked row
-  constexpr int RPW = 64 / LPR;                        // rows per wave load
-  constexpr int U = 8;                                 // wave loads in flight per batch
-  constexpr int ROWS_PER_BATCH = RPW * U;
-  constexpr int HPL = GP > LPR ? GP / LPR : 1;         // heads per lane after reduce-scatter
-  constexpr int LPH = GP < LPR ? LPR / GP : 1;         // lanes holding each head
-  constexpr float kNegInf = -__builtin_huge_valf();
-  constexpr float kInf = __builtin_huge_valf();
+__global__ __launch_bounds__(kThreads, LF_WAVES_PER_EU) void longflow_decode_kernel(DecodeParams p) {
+  using SH = Shape<D, GP>;
+  constexpr int LPR = SH::LPR, RPW = SH::RPW, U = SH::U, ROWS = SH::ROWS;
+  constexpr int HPL = SH::HPL, LPH = SH::LPH;
+  constexpr int NW = kWaves;
+  static_assert(ROWS <= kRowPad, "a wave batch may run past the split by at most kRowPad rows");
 
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -158,8 +241,8 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
   const int c = lane % LPR;   // 16-byte column chunk of the row
   const int rg = lane / LPR;  // row within the wave load
 
-  // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous run of work items so the splits of a pair share an L2.
+  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+  // contiguous run of work items so neighbouring splits share an L2.
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int per = nblk >> 3, rem = nblk & 7;
@@ -176,21 +259,36 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
   const LdsLayout L = lds_layout(D, GP, p.split_len);
   float* lg = reinterpret_cast<float*>(smem + L.logits);
   uint8_t* mk = smem + L.mask;
-  float* red = reinterpret_cast<float*>(smem + L.scratch);  // [kWaves][GP]
-  float* stat_m = red + kWaves * GP;                          // [GP]
-  float* stat_il = stat_m + GP;                               // [GP] 1 / L
-  uint64_t* best_w = reinterpret_cast<uint64_t*>(stat_il + GP);  // [kWaves], 8-byte aligned
-  int* flag = reinterpret_cast<int*>(best_w + kWaves);
+  float* red = reinterpret_cast<float*>(smem + L.scratch);     // [NW][GP]
+  float* stat_m = red + NW * GP;                                 // [GP]
+  float* stat_il = stat_m + GP;                                  // [GP] 1 / L
+  uint64_t* best_w = reinterpret_cast<uint64_t*>(stat_il + GP);  // [NW]
+  int* red_i = reinterpret_cast<int*>(best_w + NW);              // [NW]
 
   const size_t row0 = (size_t)pair * p.S;  // first cache row of this pair
-  const uint16_t* kp = p.k + row0 * D;
-  const uint16_t* vp = p.v + row0 * D;
+  const uint16_t* krows = p.k + (row0 + s0) * D;
+  const uint16_t* vrows = p.v + (row0 + s0) * D;
   const uint8_t* mrow = p.mask + (size_t)b * p.S;
   const uint16_t* nk = p.new_k + (size_t)pair * D;
   const uint16_t* nv = p.new_v + (size_t)pair * D;
 
-  // ---- setup: slot write (Figure 2, Left panel) and mask staging
-  int prev = p.prev[pair];
+  // ---- setup: queries, slot write (Figure 2, Left panel), mask staging
+  // The group's queries stay packed bf16; the logit scale (times log2 e) is
+  // applied to the reduced dot products.  Padded heads (h >= G) get q = 0 and
+  // their results are never stored.
+  uint4 qx[GP];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    const int hh = h < p.G ? h : 0;
+    const uint4 x = reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G + hh) * D)[c];
+    qx[h] = h < p.G ? x : make_uint4(0, 0, 0, 0);
+  }
+  const uint4 nkx = reinterpret_cast<const uint4*>(nk)[c];
+  const uint4 nvx = reinterpret_cast<const uint4*>(nv)[c];
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(krows, (uint32_t)n * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vrows, (uint32_t)n * D * 2);
+
+  const int prev = p.prev[pair];
   int prev_local = -1;  // split-relative row served from new_k/new_v
   if (prev != -1) {
     if (prev < 0 || prev >= p.S) {
@@ -206,9 +304,13 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
       if (tid == 0 && mrow[prev] == 0) atomicOr(p.status, LF_DEV_WRITE_MASKED);
     }
   }
+  // Mask of the split into LDS, zero-padded past its end; n_eff = one past
+  // the last valid row, so trailing masked rows are never streamed.
+  int last_valid = -1;
   {
     const uint8_t* src = mrow + s0;
-    for (int base = 0; base < n; base += kThreads * 8) {
+    const int npad = n + kRowPad;
+    for (int base = 0; base < npad; base += kThreads * 8) {
       uint8_t t8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -218,85 +320,46 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = base + u * kThreads + tid;
-        if (i < n) mk[i] = t8[u];
+        if (i < npad) mk[i] = t8[u];
+        if (t8[u] != 0) last_valid = i;
       }
     }
-  }
-
-  // Queries of the group, pre-scaled into the log2 domain.  Padded heads
-  // (h >= G) get q = 0; their results are never stored.
-  float qf[GP][8];
 #pragma unroll
-  for (int h = 0; h < GP; ++h) {
-    if (h < p.G) {
-      const uint4 x = reinterpret_cast<const uint4*>(
-          p.q + ((size_t)b * p.Hq + (size_t)j * p.G + h) * D)[c];
-      bf16x8_to_f32(x, qf[h]);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qf[h][k] *= p.qscale;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qf[h][k] = 0.f;
-    }
+    for (int m = 1; m < 64; m <<= 1) last_valid = max(last_valid, __shfl_xor(last_valid, m));
+    if (lane == 0) red_i[wave] = last_valid;
   }
   __syncthreads();
+  int n_eff = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) n_eff = max(n_eff, red_i[w] + 1);
 
-  // ---- phase K: logits into LDS
+  const int stride = NW * ROWS;
+
+  // ---- phase K: logits into LDS (rows past n_eff within the last batch get -inf)
+  // Every lane of a head's lane group holds the same reduced logit, so all of
+  // them store it (same value, same address): no branch in the loop body.
   const int hbase = GP <= LPR ? c / LPH : c * HPL;
-  const bool writer = (c % LPH) == 0;
   float mx[HPL];
 #pragma unroll
   for (int i = 0; i < HPL; ++i) mx[i] = kNegInf;
-
-  for (int r0 = wave * ROWS_PER_BATCH; r0 < n; r0 += kWaves * ROWS_PER_BATCH) {
-    uint4 kx[U];
-    bool ok[U];
-    bool any = false;
+  for (int r0 = wave * ROWS; r0 < n_eff; r0 += stride) {
+    uint4 buf[U];
+    const uint32_t ok = load_batch<D, U, RPW>(buf, krs, nkx, prev_local, mk, r0, rg, c, n);
+    float* lrow = lg + (r0 + rg) * GP + hbase;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = r0 + u * RPW + rg;
-      ok[u] = r < n && mk[r] != 0;
-      any |= ok[u];
-    }
-    if (__ballot(any) == 0) {  // every row of this batch is masked or past the end
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * RPW + rg;
-        if (writer && r < n) {
-#pragma unroll
-          for (int i = 0; i < HPL; ++i) lg[r * GP + hbase + i] = kNegInf;
-        }
-      }
-      continue;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = r0 + u * RPW + rg;
-      const uint16_t* src = (r == prev_local) ? nk : kp + (size_t)(s0 + r) * D;
-      kx[u] = ok[u] ? reinterpret_cast<const uint4*>(src)[c] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[8];
-      bf16x8_to_f32(kx[u], kf);
       float a[GP];
 #pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) s = fmaf(qf[h][k], kf[k], s);
-        a[h] = s;
-      }
+      for (int h = 0; h < GP; ++h) a[h] = dot8_bf16(buf[u], qx[h], 0.f);
       reduce_scatter<LPR / 2, GP>(a, c);
-      const int r = r0 + u * RPW + rg;
-      if (writer && r < n) {
+      const bool valid = (ok >> u) & 1u;
 #pragma unroll
-        for (int i = 0; i < HPL; ++i) {
-          const float val = ok[u] ? a[i] : kNegInf;
-          lg[r * GP + hbase + i] = val;
-          mx[i] = fmaxf(mx[i], val);
-        }
+      for (int i = 0; i < HPL; ++i) {
+        const float val = valid ? a[i] * p.qscale : kNegInf;
+        lrow[u * RPW * GP + i] = val;
+        mx[i] = fmaxf(mx[i], val);
       }
+      LF_ROW_FENCE();
     }
   }
 
@@ -307,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
 #pragma unroll
     for (int m = LPR; m < 64; m <<= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], m));
   }
-  if (rg == 0 && writer) {
+  if (rg == 0 && (c % LPH) == 0) {
 #pragma unroll
     for (int i = 0; i < HPL; ++i) red[wave * GP + hbase + i] = mx[i];
   }
@@ -315,11 +378,10 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
   if (tid < GP) {
     float m = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, red[w * GP + tid]);
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, red[w * GP + tid]);
     stat_m[tid] = m;
   }
   __syncthreads();
-
   {
     // thread -> (head tid % GP, rows tid / GP + k * kThreads / GP):
     // consecutive threads touch consecutive LDS words and workspace floats.
@@ -327,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
     const float mh = stat_m[h];
     float lsum = 0.f;
     float* wl = SPLIT ? p.ws_logit + (row0 + s0) * GP : nullptr;
-    for (int r = tid / GP; r < n; r += kThreads / GP) {
+    for (int r = tid / GP; r < n_eff; r += kThreads / GP) {
       const float s = lg[r * GP + h];
       const float e = (s == kNegInf) ? 0.f : exp2f(s - mh);
       lg[r * GP + h] = e;
@@ -336,13 +398,13 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
     }
 #pragma unroll
     for (int m = GP; m < 64; m <<= 1) lsum += __shfl_xor(lsum, m);
-    __syncthreads();  // every wave is done reading `red` (maxima)
+    __syncthreads();  // every wave is done with the maxima in `red`
     if (lane < GP) red[wave * GP + lane] = lsum;
     __syncthreads();
     if (tid < GP) {
       float l = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) l += red[w * GP + tid];
+      for (int w = 0; w < NW; ++w) l += red[w * GP + tid];
       stat_il[tid] = l > 0.f ? 1.0f / l : 0.f;
       if (SPLIT) {
         float* ml = p.part_ml + (((size_t)pair * nsplit + sp) * GP + tid) * 2;
@@ -356,76 +418,62 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
   // ---- phase V: O accumulators, |v|_1, and (single split) scores
   float il[GP];
 #pragma unroll
-  for (int h = 0; h < GP; ++h) il[h] = stat_il[h];
+  for (int h = 0; h < GP; ++h) il[h] = (h < p.G) ? stat_il[h] : 0.f;
   float acc[GP][8];
 #pragma unroll
   for (int h = 0; h < GP; ++h)
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[h][k] = 0.f;
   uint64_t best = kNoCandidate;
-  float* score_row = p.scores + row0 + s0;
-  float* vn_row = SPLIT ? p.ws_vnorm + row0 + s0 : nullptr;
 
-  for (int r0 = wave * ROWS_PER_BATCH; r0 < n; r0 += kWaves * ROWS_PER_BATCH) {
-    uint4 vx[U];
-    bool ok[U];
-    bool any = false;
+  // Each row's score (single split) or |v|_1 (several splits) goes into the
+  // LDS word that held the row's first logit, written by all lanes of the row
+  // group (same value), and leaves for HBM in one coalesced pass afterwards.
+  for (int r0 = wave * ROWS; r0 < n_eff; r0 += stride) {
+    uint4 buf[U];
+    const uint32_t ok = load_batch<D, U, RPW>(buf, vrs, nvx, prev_local, mk, r0, rg, c, n);
+    float* lrow = lg + (r0 + rg) * GP;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = r0 + u * RPW + rg;
-      ok[u] = r < n && mk[r] != 0;
-      any |= ok[u];
-    }
-    if (__ballot(any) == 0) {
-      if (!SPLIT) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int r = r0 + u * RPW + rg;
-          if (c == 0 && r < n) score_row[r] = kInf;
-        }
-      }
-      continue;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = r0 + u * RPW + rg;
-      const uint16_t* src = (r == prev_local) ? nv : vp + (size_t)(s0 + r) * D;
-      vx[u] = ok[u] ? reinterpret_cast<const uint4*>(src)[c] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = r0 + u * RPW + rg;
+      const bool valid = (ok >> u) & 1u;
       float vf[8];
-      bf16x8_to_f32(vx[u], vf);
+      bf16x8_to_f32(buf[u], vf);
       float e[GP];
 #pragma unroll
-      for (int h = 0; h < GP; ++h) e[h] = ok[u] ? lg[r * GP + h] : 0.f;
+      for (int h = 0; h < GP; ++h) {
+        const float x = lrow[u * RPW * GP + h];  // padded: in range even past the split
+        e[h] = valid ? x : 0.f;
+      }
 #pragma unroll
-      for (int h = 0; h < GP; ++h)
+      for (int h = 0; h < GP; ++h) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(e[h], vf[k], acc[h][k]);
+        pin8(acc[h]);
+      }
       float vn = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) vn += fabsf(vf[k]);
       vn = allreduce_sum<LPR / 2>(vn);
-      if (c == 0 && r < n) {
-        if (SPLIT) {
-          if (ok[u]) vn_row[r] = vn;
-        } else {
-          float sc = kInf;
-          if (ok[u]) {
-            float ps = 0.f;
+      if (SPLIT) {
+        lrow[u * RPW * GP] = vn;
+      } else {
+        float ps = 0.f;
 #pragma unroll
-            for (int h = 0; h < GP; ++h)
-              if (h < p.G) ps = fmaf(e[h], il[h], ps);
-            sc = vn * ps;
-            const uint64_t cand = pack_candidate(sc, s0 + r);
-            best = cand < best ? cand : best;
-          }
-          score_row[r] = sc;
-        }
+        for (int h = 0; h < GP; ++h) ps = fmaf(e[h], il[h], ps);
+        const float sc = valid ? vn * ps : kInf;
+        const uint64_t cand = valid ? pack_candidate(sc, s0 + r0 + u * RPW + rg) : kNoCandidate;
+        best = cand < best ? cand : best;
+        lrow[u * RPW * GP] = sc;
       }
+      LF_ROW_FENCE();
     }
+  }
+  __syncthreads();
+  {
+    // Rows at or past n_eff are all masked: score +inf, no |v|_1 needed.
+    float* dst = SPLIT ? p.ws_vnorm + row0 + s0 : p.scores + row0 + s0;
+    const int lim = SPLIT ? n_eff : n;
+    for (int r = tid; r < lim; r += kThreads) dst[r] = r < n_eff ? lg[r * GP] : kInf;
   }
 
   // ---- O: fold the row groups of each wave, then the waves through LDS
@@ -435,17 +483,17 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
     for (int k = 0; k < 8; ++k)
 #pragma unroll
       for (int m = LPR; m < 64; m <<= 1) acc[h][k] += __shfl_xor(acc[h][k], m);
-  __syncthreads();  // logits region is reused below
-  float* ored = lg;  // [kWaves][GP][D]
+  if (!SPLIT) {
+    best = wave_min_u64(best);
+    if (lane == 0) best_w[wave] = best;
+  }
+  __syncthreads();  // the logits region is reused below
+  float* ored = lg;  // [NW][GP][D]
   if (rg == 0) {
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
       for (int k = 0; k < 8; ++k) ored[(wave * GP + h) * D + c * 8 + k] = acc[h][k];
-  }
-  if (!SPLIT) {
-    best = wave_min_u64(best);
-    if (lane == 0) best_w[wave] = best;
   }
   __syncthreads();
 
@@ -455,42 +503,54 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
       if (h >= p.G) continue;
       float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) o += ored[w * GP * D + idx];
+      for (int w = 0; w < NW; ++w) o += ored[w * GP * D + idx];
       p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] =
           f32_to_bf16_rne(o * stat_il[h]);
     }
     if (tid == 0) {
       uint64_t m = best_w[0];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) m = best_w[w] < m ? best_w[w] : m;
+      for (int w = 1; w < NW; ++w) m = best_w[w] < m ? best_w[w] : m;
       p.evict[pair] = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
     }
-    return;
-  }
-
-  // ---- several splits: publish partials, the last split combines
-  {
+  } else {
     float* po = p.part_o + ((size_t)pair * nsplit + sp) * GP * D;
     for (int idx = tid; idx < GP * D; idx += kThreads) {
       float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) o += ored[w * GP * D + idx];
+      for (int w = 0; w < NW; ++w) o += ored[w * GP * D + idx];
       po[idx] = o;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t done = atomicAdd(p.counters + pair, 1u);
-    *flag = (done == (uint32_t)(nsplit - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (*flag == 0) return;
-  __threadfence();
+}
 
-  // Global softmax statistics of the pair from the split partials.
+// ------------------------------------------------------------ combine kernel
+//
+// One workgroup per (b, j) pair after a split decode: the global max M_h and
+// sum L_h from the split partials, O = sum_s acc_s * exp2(m_s - M_h) / L_h,
+// then score_i = |v_i|_1 * sum_h exp2(s_hi - M_h) / L_h for every valid slot
+// (+inf elsewhere) and the lowest-index argmin.
+
+constexpr int kCombineThreads = 256;
+
+template <int D, int GP>
+__global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(DecodeParams p) {
+  constexpr int NWC = kCombineThreads / 64;
+  constexpr int R = 4;  // rows per thread per iteration
+  __shared__ float stat_m[GP], stat_il[GP];
+  __shared__ uint64_t best_w[NWC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int pair = blockIdx.x;
+  const int b = pair / p.Hkv;
+  const int j = pair - b * p.Hkv;
+  const int nsplit = p.nsplit;
+  const float* ml = p.part_ml + (size_t)pair * nsplit * GP * 2;
+  const float* po = p.part_o + (size_t)pair * nsplit * GP * D;
+
   if (tid < GP) {
-    const float* ml = p.part_ml + (size_t)pair * nsplit * GP * 2;
     float m = kNegInf;
     for (int s = 0; s < nsplit; ++s) m = fmaxf(m, ml[(s * GP + tid) * 2]);
     float l = 0.f;
@@ -505,47 +565,77 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
   }
   __syncthreads();
 
-  {
-    const float* ml = p.part_ml + (size_t)pair * nsplit * GP * 2;
-    const float* po = p.part_o + (size_t)pair * nsplit * GP * D;
-    for (int idx = tid; idx < GP * D; idx += kThreads) {
-      const int h = idx / D;
-      if (h >= p.G) continue;
-      const float m = stat_m[h];
-      float o = 0.f;
-      if (m != kNegInf) {
-        for (int s = 0; s < nsplit; ++s) {
-          const float ms = ml[(s * GP + h) * 2];
-          if (ms != kNegInf) o += po[(size_t)s * GP * D + idx] * exp2f(ms - m);
-        }
+  for (int idx = tid; idx < GP * D; idx += kCombineThreads) {
+    const int h = idx / D;
+    if (h >= p.G) continue;
+    const float m = stat_m[h];
+    float o = 0.f;
+    if (m != kNegInf) {
+      for (int s = 0; s < nsplit; ++s) {
+        const float ms = ml[(s * GP + h) * 2];
+        if (ms != kNegInf) o += po[(size_t)s * GP * D + idx] * exp2f(ms - m);
       }
-      p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] =
-          f32_to_bf16_rne(o * stat_il[h]);
     }
+    p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] =
+        f32_to_bf16_rne(o * stat_il[h]);
   }
 
   float gm[GP], gil[GP];
 #pragma unroll
   for (int h = 0; h < GP; ++h) {
     gm[h] = stat_m[h];
-    gil[h] = stat_il[h];
+    gil[h] = h < p.G ? stat_il[h] : 0.f;
   }
-  best = kNoCandidate;
+  const size_t row0 = (size_t)pair * p.S;
   const float* wl = p.ws_logit + row0 * GP;
   const float* wv = p.ws_vnorm + row0;
+  const uint8_t* mrow = p.mask + (size_t)b * p.S;
   float* sr = p.scores + row0;
-  for (int r = tid; r < p.S; r += kThreads) {
-    float sc = kInf;
-    if (mrow[r] != 0) {
-      float ps = 0.f;
+  uint64_t best = kNoCandidate;
+  for (int base = 0; base < p.S; base += kCombineThreads * R) {
+    bool valid[R];
+    float vn[R];
+    float s[R][GP];
 #pragma unroll
-      for (int h = 0; h < GP; ++h)
-        if (h < p.G) ps = fmaf(exp2f(wl[(size_t)r * GP + h] - gm[h]), gil[h], ps);
-      sc = wv[r] * ps;
-      const uint64_t cand = pack_candidate(sc, r);
-      best = cand < best ? cand : best;
+    for (int u = 0; u < R; ++u) {
+      const int r = base + u * kCombineThreads + tid;
+      valid[u] = r < p.S && mrow[r] != 0;
     }
-    sr[r] = sc;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int r = base + u * kCombineThreads + tid;
+      vn[u] = valid[u] ? wv[r] : 0.f;
+#pragma unroll
+      for (int h4 = 0; h4 < GP; h4 += 4) {
+        if constexpr (GP >= 4) {
+          const float4 x = valid[u] ? reinterpret_cast<const float4*>(wl + (size_t)r * GP + h4)[0]
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+          s[u][h4] = x.x;
+          s[u][h4 + 1] = x.y;
+          s[u][h4 + 2] = x.z;
+          s[u][h4 + 3] = x.w;
+        }
+      }
+      if constexpr (GP < 4) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) s[u][h] = valid[u] ? wl[(size_t)r * GP + h] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int r = base + u * kCombineThreads + tid;
+      if (r >= p.S) continue;
+      float sc = kInf;
+      if (valid[u]) {
+        float ps = 0.f;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) ps = fmaf(exp2f(s[u][h] - gm[h]), gil[h], ps);
+        sc = vn[u] * ps;
+        const uint64_t cand = pack_candidate(sc, r);
+        best = cand < best ? cand : best;
+      }
+      sr[r] = sc;
+    }
   }
   best = wave_min_u64(best);
   if (lane == 0) best_w[wave] = best;
@@ -553,9 +643,8 @@ __global__ __launch_bounds__(kThreads) void longflow_decode_kernel(DecodeParams 
   if (tid == 0) {
     uint64_t m = best_w[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = best_w[w] < m ? best_w[w] : m;
+    for (int w = 1; w < NWC; ++w) m = best_w[w] < m ? best_w[w] : m;
     p.evict[pair] = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
-    p.counters[pair] = 0;  // ready for the next call
   }
 }
 
@@ -569,12 +658,17 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
 
 template <int D, int GP>
 hipError_t launch_dg(const DecodeParams& prm, int nblocks, size_t lds, hipStream_t stream) {
-  if (prm.nsplit > 1)
+  if (prm.nsplit > 1) {
     hipLaunchKernelGGL((longflow_decode_kernel<D, GP, true>), dim3(nblocks), dim3(kThreads), lds,
                        stream, prm);
-  else
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((longflow_combine_kernel<D, GP>), dim3(nblocks / prm.nsplit),
+                       dim3(kCombineThreads), 0, stream, prm);
+  } else {
     hipLaunchKernelGGL((longflow_decode_kernel<D, GP, false>), dim3(nblocks), dim3(kThreads), lds,
                        stream, prm);
+  }
   return hipGetLastError();
 }
 

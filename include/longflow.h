@@ -103,8 +103,8 @@ int lf_check_shape(int B, int Hq, int Hkv, int d, int S);
 /* Host-only choice of the number of slot splits per (sequence, KV head) for
  * a device with `num_cus` compute units.  Writes the count to *nsplit.  A
  * split count of 1 keeps the whole step of a (b, j) pair in one workgroup;
- * larger counts split the slots (flash-decoding) and combine the partial
- * softmax statistics in the same launch. */
+ * larger counts split the slots (flash-decoding) and add a combine kernel
+ * that rescales the partial softmax statistics to the true softmax. */
 int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nsplit);
 
 /* Host-only workspace size in bytes for an explicit split count (>= 1). */
@@ -113,10 +113,9 @@ int lf_workspace_size(int B, int Hq, int Hkv, int d, int S, int nsplit, size_t* 
 /* Compute units of the current HIP device (cached per device). */
 int lf_device_num_cus(int* num_cus);
 
-/* Zero the workspace's status word and combine counters with a fill kernel
- * enqueued on `stream`.  Required once before the first longflow_decode on a
- * workspace whose contents are not already zero; every completed call leaves
- * the counters at zero again. */
+/* Zero the workspace (its status word included) with a fill kernel enqueued
+ * on `stream`.  Needed only to clear recorded LF_DEV_* bits: no other
+ * workspace content carries over from one call to the next. */
 int lf_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only argument validation, exactly the checks longflow_decode_nsplit

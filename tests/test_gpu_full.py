@@ -24,7 +24,7 @@ def _device():
 
 def sample_pairs(wl):
     B, H = wl.B, wl.Hkv
-    pairs = {(0, 0), (B - 1, H - 1), (B // 2, H // 2), (B // 3, H - 2), (min(1, B - 1), 1)}
+    pairs = {(0, 0), (B - 1, H - 1), (B // 2, H // 2), (B // 3, max(0, H - 2)), (min(1, B - 1), min(1, H - 1))}
     if wl.kind == "ragged":
         lens = [W.valid_length(wl, b) for b in range(B)]
         pairs |= {(lens.index(min(lens)), 0), (lens.index(max(lens)), H - 1)}
