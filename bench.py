@@ -13,7 +13,6 @@ device.  Prints one JSON line.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,20 +27,10 @@ METRIC = "fused decode-attn+evict: KV GB/s (% HBM peak), steps/s at B=128, 3200 
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kv_05_amd", "csrc", n)
-                  for n in ("longflow_kernels.hip", "layout.h", "launch.h", "longflow_api.cpp")]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_hash():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def valid_slots(mask):
@@ -69,7 +58,8 @@ def measured_traffic(workload, nsplit):
             rec = json.load(f).get(f"{workload}/nsplit{nsplit}")
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_hash") != kernel_hash():
+    from decode_attention_kv_05_amd.build import source_hash
+    if not rec or rec.get("kernel_hash") != source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -114,6 +104,9 @@ def main():
     ap.add_argument("--nsplit", type=int, default=None, help="slot splits per pair (default: library plan)")
     ap.add_argument("--cpu-pairs", type=int, default=384, help="oracle sample size for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times "
+                         "(calibrates HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -136,6 +129,14 @@ def main():
         raise RuntimeError("no HIP device visible")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        src = torch.full((args.copy_probe,), 7, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 5}), flush=True)
+        return
     props = torch.cuda.get_device_properties(dev)
     wl = W.WORKLOADS[args.workload]
     K, Wm = args.steps, args.warmup

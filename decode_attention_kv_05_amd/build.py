@@ -20,6 +20,17 @@ SOURCES = [os.path.join(CSRC, "longflow_api.cpp"), os.path.join(CSRC, "longflow_
 ARCH = "gfx950"
 
 
+def source_hash():
+    """Short hash of the kernel and host sources (identifies a kernel build)."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in sorted(SOURCES + [os.path.join(CSRC, n) for n in ("layout.h", "launch.h")]
+                       + [os.path.join(INCLUDE, "longflow.h")]):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):

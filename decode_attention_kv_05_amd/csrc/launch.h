@@ -23,11 +23,12 @@ struct DecodeParams {
   float* part_o;          // workspace: [pairs][nsplit][GP][d]
   float* ws_logit;        // workspace: [pairs][S][GP]
   float* ws_vnorm;        // workspace: [pairs][S]
+  uint64_t* cand;         // workspace: [pairs][chunks] packed (score, slot) minima
   int Hq, Hkv, G, S, nsplit, split_len;
   float qscale;           // logit scale times log2(e)
 };
 
-hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nblocks, size_t lds,
+hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
                          hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 

@@ -16,21 +16,31 @@ namespace lf {
 
 constexpr int kMaxGroup = 8;          // query heads per KV head supported
 // Tuning knobs of the decode kernel; the defaults are the shipped choice.
-#ifndef LF_WAVES
-#define LF_WAVES 8  // wavefronts per workgroup
+#ifndef LF_WAVES_SMALL_LDS
+#define LF_WAVES_SMALL_LDS 8  // wavefronts per workgroup when two workgroups fit a CU's LDS
+#endif
+#ifndef LF_WAVES_LARGE_LDS
+#define LF_WAVES_LARGE_LDS 16  // wavefronts per workgroup when one workgroup fills the LDS
 #endif
 #ifndef LF_UNROLL
-#define LF_UNROLL 8  // 16-byte row loads per lane per batch (halved for groups of 8)
+#define LF_UNROLL 4  // 16-byte row loads per lane per batch
 #endif
-#ifndef LF_WAVES_PER_EU
-#define LF_WAVES_PER_EU 4  // occupancy hint given to the register allocator
+// Occupancy hint given to the register allocator, by padded group size:
+// waves per SIMD the kernel must fit (512 VGPRs per lane / waves).
+#ifndef LF_WAVES_PER_EU_SMALL
+#define LF_WAVES_PER_EU_SMALL 5  // groups of up to 4 query heads
+#endif
+#ifndef LF_WAVES_PER_EU_LARGE
+#define LF_WAVES_PER_EU_LARGE 4  // groups of 8
 #endif
 
-constexpr int kWaves = LF_WAVES;      // wavefronts per workgroup
-constexpr int kThreads = kWaves * 64; // threads per workgroup
+constexpr int kMaxWaves = LF_WAVES_LARGE_LDS > LF_WAVES_SMALL_LDS ? LF_WAVES_LARGE_LDS : LF_WAVES_SMALL_LDS;
 constexpr int kMaxSplits = 1024;      // slot splits per (sequence, KV head)
 // LDS bytes a workgroup may spend on the logits of its slot range.
-constexpr size_t kLogitLdsBudget = 56 * 1024;
+#ifndef LF_LOGIT_LDS_KB
+#define LF_LOGIT_LDS_KB 136
+#endif
+constexpr size_t kLogitLdsBudget = (size_t)LF_LOGIT_LDS_KB * 1024;
 
 LF_HD inline int padded_group(int g) {
   int p = 1;
@@ -54,8 +64,13 @@ struct WorkspaceLayout {
   size_t part_o;    // float [pairs][nsplit][GP][d]: split output accumulators
   size_t logit;     // float [pairs][S][GP]: log2-domain logits
   size_t vnorm;     // float [pairs][S]: |v|_1 per slot
+  size_t cand;      // uint64 [pairs][combine chunks]: per-chunk (score, slot) minima
   size_t total;
 };
+
+// Slots per workgroup of the split combine.
+constexpr int kCombineSlots = 2048;
+LF_HD inline int combine_chunks(int S) { return (S + kCombineSlots - 1) / kCombineSlots; }
 
 LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int gp, int nsplit_eff) {
   WorkspaceLayout w{};
@@ -71,8 +86,10 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
     off = align_up(off + pairs * (size_t)S * gp * 4, 256);
     w.vnorm = off;
     off = align_up(off + pairs * (size_t)S * 4, 256);
+    w.cand = off;
+    off = align_up(off + pairs * (size_t)combine_chunks(S) * 8, 256);
   } else {
-    w.part_ml = w.part_o = w.logit = w.vnorm = off;
+    w.part_ml = w.part_o = w.logit = w.vnorm = w.cand = off;
   }
   w.total = off;
   return w;
@@ -91,10 +108,17 @@ constexpr size_t kScratchBytes = 1024;
 // logit arrays are padded by this much so those reads need no bounds check.
 constexpr int kRowPad = 128;
 
-LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len) {
+// Wavefronts per decode workgroup for a split: a workgroup whose logits
+// leave room for a second one on the CU gets fewer waves, so that two of
+// them (which reach their barriers independently) share the CU.
+LF_HD inline int decode_waves(int gp, int split_len) {
+  return (size_t)(split_len + kRowPad) * gp * 4 > 64 * 1024 ? LF_WAVES_LARGE_LDS : LF_WAVES_SMALL_LDS;
+}
+
+LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len, int nw) {
   LdsLayout l{};
   size_t logits = align_up((size_t)(split_len + kRowPad) * gp * 4, 16);
-  size_t ored = (size_t)kWaves * gp * d * 4;
+  size_t ored = (size_t)nw * gp * d * 4;
   l.logits = 0;
   size_t off = logits > ored ? logits : ored;
   l.mask = off;
@@ -102,6 +126,17 @@ LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len) {
   l.scratch = off;
   l.total = off + kScratchBytes;
   return l;
+}
+
+// LDS of one compute unit on gfx950; a workgroup may use all of it.
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+
+// Longest split whose logits fit the budget and whose whole LDS layout fits
+// the compute unit.
+LF_HD inline int max_split_len(int d, int gp) {
+  int len = (int)(kLogitLdsBudget / ((size_t)gp * 4));
+  while (len > 0 && lds_layout(d, gp, len, kMaxWaves).total > kMaxLdsBytes) len -= 64;
+  return len;
 }
 
 }  // namespace lf

@@ -27,7 +27,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-int max_split_len(int gp) { return (int)(lf::kLogitLdsBudget / ((size_t)gp * 4)); }
 
 }  // namespace
 
@@ -67,14 +66,18 @@ int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nspli
   const int gp = lf::padded_group(Hq / Hkv);
   const int64_t pairs = (int64_t)B * Hkv > 0 ? (int64_t)B * Hkv : 1;
   // The logits of a split must fit the LDS budget.
-  const int64_t need = ((int64_t)S + max_split_len(gp) - 1) / max_split_len(gp);
-  // Aim for about four workgroups per compute unit, but do not cut splits
-  // below 256 slots just to get there.
-  const int64_t target = (4LL * num_cus + pairs - 1) / pairs;
-  int64_t n = target;
-  const int64_t cap = ((int64_t)S + 255) / 256;
-  if (n > cap) n = cap;
-  if (n < need) n = need;
+  const int64_t need = ((int64_t)S + lf::max_split_len(d, gp) - 1) / lf::max_split_len(d, gp);
+  int64_t n = need;
+  // One workgroup per pair keeps the whole step on chip (no workspace round
+  // trip, no combine launch); use it when there are enough pairs to give
+  // every compute unit work.  Otherwise split the slots until there are
+  // about two workgroups per compute unit, but not below 256 slots a split.
+  if (!(need == 1 && pairs >= num_cus)) {
+    const int64_t target = (2LL * num_cus + pairs - 1) / pairs;
+    const int64_t cap = ((int64_t)S + 255) / 256;
+    if (target > n) n = target < cap ? target : cap;
+    if (n < need) n = need;
+  }
   if (n < 1) n = 1;
   if (n > lf::kMaxSplits) return LF_E_SHAPE;
   int len, eff;
@@ -144,7 +147,7 @@ int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale, const void* q
   const int gp = lf::padded_group(Hq / Hkv);
   int len, eff;
   lf::split_geometry(S, nsplit, &len, &eff);
-  if (len > max_split_len(gp)) return LF_E_NSPLIT;
+  if (len > lf::max_split_len(d, gp)) return LF_E_NSPLIT;
   if ((int64_t)B * Hkv * eff > INT_MAX) return LF_E_NSPLIT;
 
   const size_t pairs = (size_t)B * Hkv;
@@ -210,6 +213,7 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
   prm.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   prm.ws_logit = reinterpret_cast<float*>(ws + wl.logit);
   prm.ws_vnorm = reinterpret_cast<float*>(ws + wl.vnorm);
+  prm.cand = reinterpret_cast<uint64_t*>(ws + wl.cand);
   prm.Hq = Hq;
   prm.Hkv = Hkv;
   prm.G = G;
@@ -220,8 +224,9 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
   prm.qscale = scale * 1.4426950408889634f;
 
   const int nblocks = B * Hkv * eff;
-  const size_t lds = lf::lds_layout(d, gp, len).total;
-  return lf::launch_decode(prm, d, gp, nblocks, lds, static_cast<hipStream_t>(stream)) ==
+  const int nw = lf::decode_waves(gp, len);
+  const size_t lds = lf::lds_layout(d, gp, len, nw).total;
+  return lf::launch_decode(prm, d, gp, nw, nblocks, lds, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? LF_OK
              : LF_E_HIP;

@@ -6,8 +6,8 @@
 // choice, attend, return the next slot; Middle: K/V and mask streamed from HBM
 // by block; Right: P.V split into G then O, score from G).
 //
-// decode kernel: one workgroup (8 waves) per slot range ("split") of one
-// (sequence b, KV head j) pair.
+// decode kernel: one workgroup (8 or 16 waves) per slot range ("split") of
+// one (sequence b, KV head j) pair.
 //
 //   setup    the split that owns prev_slot copies new_k/new_v into that cache
 //            row and reads the row from new_k/new_v for the rest of the step;
@@ -28,9 +28,9 @@
 //            phase V, O = acc / L, and the argmin over packed (score bits,
 //            slot) words gives the evicted slot.
 //            several splits: each split writes its (M, L, acc) partials, the
-//            logits and |v|_1 to the workspace; the combine kernel launched
-//            right after on the same stream rescales them to the true
-//            softmax.  The kernel boundary orders the two, so no cross-
+//            logits and |v|_1 to the workspace; the combine and finalize
+//            kernels launched right after on the same stream rescale them
+//            to the true softmax.  The kernel boundary orders the two, so no cross-
 //            workgroup fences are needed.
 //
 // Every slot goes through the same instruction sequence, so two slots with
@@ -193,11 +193,13 @@ constexpr float kInf = __builtin_huge_valf();
 
 // ------------------------------------------------------------ decode kernel
 
+constexpr int waves_per_eu(int gp) { return gp >= 8 ? LF_WAVES_PER_EU_LARGE : LF_WAVES_PER_EU_SMALL; }
+
 template <int D, int GP>
 struct Shape {
   static constexpr int LPR = D / 8;                     // lanes per row (16 bytes each)
   static constexpr int RPW = 64 / LPR;                  // rows per wave load
-  static constexpr int U = GP >= 8 ? LF_UNROLL / 2 : LF_UNROLL;  // wave loads per batch
+  static constexpr int U = LF_UNROLL;                   // wave loads per batch
   static constexpr int ROWS = RPW * U;                  // rows per wave batch
   static constexpr int HPL = GP > LPR ? GP / LPR : 1;   // heads per lane after reduce-scatter
   static constexpr int LPH = GP < LPR ? LPR / GP : 1;   // lanes holding each head
@@ -225,12 +227,12 @@ __device__ __forceinline__ uint32_t load_batch(uint4 (&buf)[U], __amdgpu_buffer_
   return ok;
 }
 
-template <int D, int GP, bool SPLIT>
-__global__ __launch_bounds__(kThreads, LF_WAVES_PER_EU) void longflow_decode_kernel(DecodeParams p) {
+template <int D, int GP, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_kernel(DecodeParams p) {
   using SH = Shape<D, GP>;
   constexpr int LPR = SH::LPR, RPW = SH::RPW, U = SH::U, ROWS = SH::ROWS;
   constexpr int HPL = SH::HPL, LPH = SH::LPH;
-  constexpr int NW = kWaves;
+  constexpr int kThreads = NW * 64;
   static_assert(ROWS <= kRowPad, "a wave batch may run past the split by at most kRowPad rows");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kThreads, LF_WAVES_PER_EU) void longflow_decode_ker
   const int s0 = sp * p.split_len;
   const int n = min(p.S, s0 + p.split_len) - s0;
 
-  const LdsLayout L = lds_layout(D, GP, p.split_len);
+  const LdsLayout L = lds_layout(D, GP, p.split_len, NW);
   float* lg = reinterpret_cast<float*>(smem + L.logits);
   uint8_t* mk = smem + L.mask;
   float* red = reinterpret_cast<float*>(smem + L.scratch);     // [NW][GP]
@@ -524,31 +526,37 @@ __global__ __launch_bounds__(kThreads, LF_WAVES_PER_EU) void longflow_decode_ker
   }
 }
 
-// ------------------------------------------------------------ combine kernel
+// ------------------------------------------------------------ combine kernels
 //
-// One workgroup per (b, j) pair after a split decode: the global max M_h and
-// sum L_h from the split partials, O = sum_s acc_s * exp2(m_s - M_h) / L_h,
-// then score_i = |v_i|_1 * sum_h exp2(s_hi - M_h) / L_h for every valid slot
-// (+inf elsewhere) and the lowest-index argmin.
+// After a split decode.  longflow_combine_kernel: one workgroup per (pair,
+// chunk of kCombineRows slots).  It rebuilds the pair's global max M_h and sum
+// L_h from the split partials, writes score_i = |v_i|_1 * sum_h exp2(s_hi -
+// M_h) / L_h for the valid slots of its chunk (+inf elsewhere) and the
+// chunk's lowest-index minimum; chunk 0 also writes O = sum_s acc_s *
+// exp2(m_s - M_h) / L_h.  longflow_finalize_kernel then takes the minimum
+// over the chunks of each pair.
 
 constexpr int kCombineThreads = 256;
+constexpr int kCombineRowsPerThread = 8;
+constexpr int kCombineRows = kCombineThreads * kCombineRowsPerThread;
+static_assert(kCombineRows == kCombineSlots, "combine chunking must match the workspace layout");
 
 template <int D, int GP>
-__global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(DecodeParams p, int nchunk) {
   constexpr int NWC = kCombineThreads / 64;
-  constexpr int R = 4;  // rows per thread per iteration
+  constexpr int R = kCombineRowsPerThread;
   __shared__ float stat_m[GP], stat_il[GP];
   __shared__ uint64_t best_w[NWC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int pair = blockIdx.x;
+  const int pair = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x - pair * nchunk;
   const int b = pair / p.Hkv;
   const int j = pair - b * p.Hkv;
   const int nsplit = p.nsplit;
   const float* ml = p.part_ml + (size_t)pair * nsplit * GP * 2;
-  const float* po = p.part_o + (size_t)pair * nsplit * GP * D;
 
   if (tid < GP) {
     float m = kNegInf;
@@ -565,19 +573,22 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
   }
   __syncthreads();
 
-  for (int idx = tid; idx < GP * D; idx += kCombineThreads) {
-    const int h = idx / D;
-    if (h >= p.G) continue;
-    const float m = stat_m[h];
-    float o = 0.f;
-    if (m != kNegInf) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float ms = ml[(s * GP + h) * 2];
-        if (ms != kNegInf) o += po[(size_t)s * GP * D + idx] * exp2f(ms - m);
+  if (chunk == 0) {
+    const float* po = p.part_o + (size_t)pair * nsplit * GP * D;
+    for (int idx = tid; idx < GP * D; idx += kCombineThreads) {
+      const int h = idx / D;
+      if (h >= p.G) continue;
+      const float m = stat_m[h];
+      float o = 0.f;
+      if (m != kNegInf) {
+        for (int s = 0; s < nsplit; ++s) {
+          const float ms = ml[(s * GP + h) * 2];
+          if (ms != kNegInf) o += po[(size_t)s * GP * D + idx] * exp2f(ms - m);
+        }
       }
+      p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] =
+          f32_to_bf16_rne(o * stat_il[h]);
     }
-    p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] =
-        f32_to_bf16_rne(o * stat_il[h]);
   }
 
   float gm[GP], gil[GP];
@@ -591,51 +602,48 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
   const float* wv = p.ws_vnorm + row0;
   const uint8_t* mrow = p.mask + (size_t)b * p.S;
   float* sr = p.scores + row0;
-  uint64_t best = kNoCandidate;
-  for (int base = 0; base < p.S; base += kCombineThreads * R) {
-    bool valid[R];
-    float vn[R];
-    float s[R][GP];
+  const int base = chunk * kCombineRows;
+  bool valid[R];
+  float vn[R];
+  float s[R][GP];
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int r = base + u * kCombineThreads + tid;
-      valid[u] = r < p.S && mrow[r] != 0;
-    }
+  for (int u = 0; u < R; ++u) {
+    const int r = base + u * kCombineThreads + tid;
+    valid[u] = r < p.S && mrow[r] != 0;
+  }
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int r = base + u * kCombineThreads + tid;
-      vn[u] = valid[u] ? wv[r] : 0.f;
+  for (int u = 0; u < R; ++u) {
+    const int r = base + u * kCombineThreads + tid;
+    vn[u] = valid[u] ? wv[r] : 0.f;
+    if constexpr (GP >= 4) {
 #pragma unroll
       for (int h4 = 0; h4 < GP; h4 += 4) {
-        if constexpr (GP >= 4) {
-          const float4 x = valid[u] ? reinterpret_cast<const float4*>(wl + (size_t)r * GP + h4)[0]
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-          s[u][h4] = x.x;
-          s[u][h4 + 1] = x.y;
-          s[u][h4 + 2] = x.z;
-          s[u][h4 + 3] = x.w;
-        }
+        const float4 x = valid[u] ? reinterpret_cast<const float4*>(wl + (size_t)r * GP + h4)[0]
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        s[u][h4] = x.x;
+        s[u][h4 + 1] = x.y;
+        s[u][h4 + 2] = x.z;
+        s[u][h4 + 3] = x.w;
       }
-      if constexpr (GP < 4) {
+    } else {
 #pragma unroll
-        for (int h = 0; h < GP; ++h) s[u][h] = valid[u] ? wl[(size_t)r * GP + h] : 0.f;
-      }
+      for (int h = 0; h < GP; ++h) s[u][h] = valid[u] ? wl[(size_t)r * GP + h] : 0.f;
     }
+  }
+  uint64_t best = kNoCandidate;
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int r = base + u * kCombineThreads + tid;
-      if (r >= p.S) continue;
-      float sc = kInf;
-      if (valid[u]) {
-        float ps = 0.f;
+  for (int u = 0; u < R; ++u) {
+    const int r = base + u * kCombineThreads + tid;
+    float sc = kInf;
+    if (valid[u]) {
+      float ps = 0.f;
 #pragma unroll
-        for (int h = 0; h < GP; ++h) ps = fmaf(exp2f(s[u][h] - gm[h]), gil[h], ps);
-        sc = vn[u] * ps;
-        const uint64_t cand = pack_candidate(sc, r);
-        best = cand < best ? cand : best;
-      }
-      sr[r] = sc;
+      for (int h = 0; h < GP; ++h) ps = fmaf(exp2f(s[u][h] - gm[h]), gil[h], ps);
+      sc = vn[u] * ps;
+      const uint64_t cand = pack_candidate(sc, r);
+      best = cand < best ? cand : best;
     }
+    if (r < p.S) sr[r] = sc;
   }
   best = wave_min_u64(best);
   if (lane == 0) best_w[wave] = best;
@@ -644,8 +652,17 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
     uint64_t m = best_w[0];
 #pragma unroll
     for (int w = 1; w < NWC; ++w) m = best_w[w] < m ? best_w[w] : m;
-    p.evict[pair] = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
+    p.cand[(size_t)pair * nchunk + chunk] = m;
   }
+}
+
+__global__ void longflow_finalize_kernel(DecodeParams p, int pairs, int nchunk) {
+  const int pair = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pair >= pairs) return;
+  const uint64_t* c = p.cand + (size_t)pair * nchunk;
+  uint64_t m = kNoCandidate;
+  for (int i = 0; i < nchunk; ++i) m = c[i] < m ? c[i] : m;
+  p.evict[pair] = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
@@ -656,38 +673,51 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
 
 // ------------------------------------------------------------------ launch
 
-template <int D, int GP>
-hipError_t launch_dg(const DecodeParams& prm, int nblocks, size_t lds, hipStream_t stream) {
+template <int D, int GP, int NW>
+hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, hipStream_t stream) {
   if (prm.nsplit > 1) {
-    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, true>), dim3(nblocks), dim3(kThreads), lds,
+    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, true>), dim3(nblocks), dim3(NW * 64), lds,
                        stream, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((longflow_combine_kernel<D, GP>), dim3(nblocks / prm.nsplit),
-                       dim3(kCombineThreads), 0, stream, prm);
+    const int pairs = nblocks / prm.nsplit;
+    const int nchunk = combine_chunks(prm.S);
+    hipLaunchKernelGGL((longflow_combine_kernel<D, GP>), dim3(pairs * nchunk), dim3(kCombineThreads),
+                       0, stream, prm, nchunk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(longflow_finalize_kernel, dim3((pairs + 255) / 256), dim3(256), 0, stream,
+                       prm, pairs, nchunk);
   } else {
-    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, false>), dim3(nblocks), dim3(kThreads), lds,
+    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, false>), dim3(nblocks), dim3(NW * 64), lds,
                        stream, prm);
   }
   return hipGetLastError();
 }
 
+template <int D, int GP>
+hipError_t launch_dg(const DecodeParams& prm, int nw, int nblocks, size_t lds, hipStream_t stream) {
+  if (nw == LF_WAVES_LARGE_LDS) return launch_dgw<D, GP, LF_WAVES_LARGE_LDS>(prm, nblocks, lds, stream);
+  if (nw == LF_WAVES_SMALL_LDS) return launch_dgw<D, GP, LF_WAVES_SMALL_LDS>(prm, nblocks, lds, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int D>
-hipError_t launch_d(const DecodeParams& prm, int gp, int nblocks, size_t lds, hipStream_t stream) {
+hipError_t launch_d(const DecodeParams& prm, int gp, int nw, int nblocks, size_t lds, hipStream_t stream) {
   switch (gp) {
-    case 1: return launch_dg<D, 1>(prm, nblocks, lds, stream);
-    case 2: return launch_dg<D, 2>(prm, nblocks, lds, stream);
-    case 4: return launch_dg<D, 4>(prm, nblocks, lds, stream);
-    case 8: return launch_dg<D, 8>(prm, nblocks, lds, stream);
+    case 1: return launch_dg<D, 1>(prm, nw, nblocks, lds, stream);
+    case 2: return launch_dg<D, 2>(prm, nw, nblocks, lds, stream);
+    case 4: return launch_dg<D, 4>(prm, nw, nblocks, lds, stream);
+    case 8: return launch_dg<D, 8>(prm, nw, nblocks, lds, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nblocks, size_t lds,
+hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
                          hipStream_t stream) {
   switch (d) {
-    case 64: return launch_d<64>(prm, gp, nblocks, lds, stream);
-    case 128: return launch_d<128>(prm, gp, nblocks, lds, stream);
+    case 64: return launch_d<64>(prm, gp, nw, nblocks, lds, stream);
+    case 128: return launch_d<128>(prm, gp, nw, nblocks, lds, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,135 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+    python -m decode_attention_kv_05_amd.profile_summary stats DIR --workload W --command "..."
+    python -m decode_attention_kv_05_amd.profile_summary traffic --workload W --nsplit N \
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes BYTES --command "..."
+
+`stats` reads a `rocprofv3 --kernel-trace --stats --output-format csv` run and
+writes profiles/longflow_decode_<W>_kernels.txt.  `traffic` reads four
+`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (the decode benchmark
+and a plain device copy of a known size, run with `bench.py --copy-probe`),
+scales the decode kernel's per-dispatch KiB by bytes-copied / KiB-counted of
+the copy, and writes profiles/longflow_decode_<W>_traffic.txt plus an entry of
+profiles/traffic.json tagged with the hash of the kernel sources it measured
+(bench.py reports the figure only while that hash matches).
+"""
+
+import argparse
+import csv
+import glob
+import json
+import os
+import time
+
+from .build import source_hash
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE = "longflow_decode_kernel"
+COPY_HINTS = ("copy",)
+
+
+def _find(directory, suffix):
+    hits = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    return hits[0]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def counter_means(directory, counter):
+    """Mean per-dispatch value of `counter` by kernel name."""
+    sums, counts = {}, {}
+    for row in _rows(_find(directory, "counter_collection.csv")):
+        if row.get("Counter_Name") != counter:
+            continue
+        name = row["Kernel_Name"]
+        sums[name] = sums.get(name, 0.0) + float(row["Counter_Value"])
+        counts[name] = counts.get(name, 0) + 1
+    return {k: (sums[k] / counts[k], counts[k]) for k in sums}
+
+
+def _pick(means, want):
+    for name, val in means.items():
+        if want(name):
+            return name, val
+    raise KeyError(f"kernel not found among {list(means)}")
+
+
+def write_stats(args):
+    rows = _rows(_find(args.dir, "kernel_stats.csv"))
+    out = os.path.join(PROFILES, f"longflow_decode_{args.workload}_kernels.txt")
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 kernel statistics, workload {args.workload}\n")
+        f.write(f"# command: {args.command}\n")
+        f.write(f"# kernel sources: {source_hash()}  date: {time.strftime('%Y-%m-%d')}\n")
+        f.write(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel\n")
+        for r in rows:
+            f.write(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                    f"{float(r['MaxNs']) / 1e3:>10.2f} {float(r['Percentage']):>6.2f}  {r['Name'][:110]}\n")
+    print(out)
+
+
+def write_traffic(args):
+    fetch = counter_means(args.fetch, "FETCH_SIZE")
+    write = counter_means(args.write, "WRITE_SIZE")
+    cfetch = counter_means(args.copy_fetch, "FETCH_SIZE")
+    cwrite = counter_means(args.copy_write, "WRITE_SIZE")
+    is_decode = lambda n: DECODE in n
+    is_copy = lambda n: any(h in n.lower() for h in COPY_HINTS) and DECODE not in n
+    kname, (f_kib, nf) = _pick(fetch, is_decode)
+    _, (w_kib, nw) = _pick(write, is_decode)
+    cname, (cf_kib, _) = _pick(cfetch, is_copy)
+    _, (cw_kib, _) = _pick(cwrite, is_copy)
+    f_scale = args.copy_bytes / (cf_kib * 1024.0)
+    w_scale = args.copy_bytes / (cw_kib * 1024.0)
+    read_b = f_kib * 1024.0 * f_scale
+    write_b = w_kib * 1024.0 * w_scale
+    total = read_b + write_b
+    tag = f"{args.workload}/nsplit{args.nsplit}"
+    out = os.path.join(PROFILES, f"longflow_decode_{args.workload}_traffic.txt")
+    with open(out, "w") as f:
+        f.write(f"# HBM traffic of {kname[:80]} from rocprofv3 counters, workload {args.workload}, nsplit {args.nsplit}\n")
+        f.write(f"# commands: {args.command}\n")
+        f.write(f"# kernel sources: {source_hash()}  date: {time.strftime('%Y-%m-%d')}\n")
+        f.write(f"FETCH_SIZE KiB/dispatch (decode, mean of {nf}): {f_kib:.1f}\n")
+        f.write(f"WRITE_SIZE KiB/dispatch (decode, mean of {nw}): {w_kib:.1f}\n")
+        f.write(f"copy probe {cname[:60]}: {args.copy_bytes} bytes; FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB\n")
+        f.write(f"scale factors (bytes per counted byte): fetch {f_scale:.4f}, write {w_scale:.4f}\n")
+        f.write(f"HBM bytes per launch: read {read_b:.0f}, write {write_b:.0f}, total {total:.0f}\n")
+    path = os.path.join(PROFILES, "traffic.json")
+    try:
+        with open(path) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        db = {}
+    db[tag] = {"kernel_hash": source_hash(), "bytes_per_launch": round(total), "read_bytes": round(read_b),
+               "write_bytes": round(write_b), "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5)}
+    with open(path, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(out)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--workload", required=True)
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("workload", "fetch", "write", "copy_fetch", "copy_write", "command"):
+        t.add_argument("--" + k.replace("_", "-"), required=True)
+    t.add_argument("--nsplit", type=int, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    args = ap.parse_args()
+    (write_stats if args.cmd == "stats" else write_traffic)(args)
+
+
+if __name__ == "__main__":
+    main()
