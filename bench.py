@@ -64,9 +64,11 @@ def measured_traffic(workload, nsplit):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, mask, max_pairs):
-    """The fp64 oracle on a bounded sample of the same workload (first step),
-    single-threaded, scaled by valid K/V bytes to the whole step."""
+def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
+    """The fp64 oracle, single-threaded, on a bounded sample of the same
+    workload: up to `max_pairs` (sequence, KV head) pairs per step, over
+    consecutive steps until `min_seconds` of work, scaled by valid K/V bytes
+    to whole steps."""
     from threadpoolctl import threadpool_limits
 
     from decode_attention_kv_05_amd import workloads as W
@@ -75,21 +77,24 @@ def cpu_baseline(wl, mask, max_pairs):
     nb = max(1, min(wl.B, -(-max_pairs // wl.Hkv)))
     batch = list(range(nb))
     k, v, m = W.initial_cache(wl, batch)
-    q, nk, nv = W.step_inputs(wl, 0, batch)
     prev = W.first_prev_slot(wl, batch)
+    steps, busy = 0, 0.0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        decode_step(q, k, v, m, nk, nv, prev, wl.scale)
-        dt = time.perf_counter() - t0
+        while busy < min_seconds and steps < wl.steps:
+            q, nk, nv = W.step_inputs(wl, steps, batch)
+            t0 = time.perf_counter()
+            _, _, prev = decode_step(q, k, v, m, nk, nv, prev, wl.scale)
+            busy += time.perf_counter() - t0
+            steps += 1
     frac = valid_slots(m) / max(1, valid_slots(mask))
-    s_per_step = dt / frac
+    s_per_step = busy / steps / frac
     return {
         "value": round(kv_bytes(wl, mask) / s_per_step / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{nb * wl.Hkv} of {wl.B * wl.Hkv} (sequence, KV head) pairs of step 0 "
-                  f"({dt:.1f} s), scaled by valid K/V bytes; numpy fp64, BLAS limited to 1 thread",
+        "sample": f"{nb * wl.Hkv} of {wl.B * wl.Hkv} (sequence, KV head) pairs over {steps} decode steps "
+                  f"({busy:.1f} s), scaled by valid K/V bytes; numpy fp64, BLAS limited to 1 thread",
         "steps_per_s": round(1.0 / s_per_step, 6),
         "s_per_step": round(s_per_step, 3),
     }
@@ -102,7 +107,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_8b")
     ap.add_argument("--nsplit", type=int, default=None, help="slot splits per pair (default: library plan)")
-    ap.add_argument("--cpu-pairs", type=int, default=384, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--cpu-pairs", type=int, default=1024, help="oracle sample: pairs per step for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times "

@@ -60,9 +60,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// Cache policy of the K/V stream: rows are read once per step, so they may
+// be marked non-temporal (nt) to leave the caches to everything else.
+#ifndef LF_NT_LOADS
+#define LF_NT_LOADS 1
+#endif
+#ifndef LF_STREAM_POLICY
+#define LF_STREAM_POLICY 2  // cache-policy bits of the buffer load: nt
+#endif
+constexpr int kStreamPolicy = LF_NT_LOADS ? LF_STREAM_POLICY : 0;
+
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
-  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 0);
+  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, kStreamPolicy);
   return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// Sum of the absolute values of the 8 bf16 in a 16-byte chunk, in fp32
+// (sign bits cleared, then dotted with (1, 1)).
+__device__ __forceinline__ float abs_sum8_bf16(const uint4& a) {
+  const uint32_t ones = 0x3f803f80u;  // bf16 (1.0, 1.0)
+  float s = 0.f;
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
+  return s;
+}
+
+// bf16 pair (lo, hi) from two fp32 values, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // fp32 sum of the 8 products of two rows of 8 bf16 values, plus `acc`
@@ -192,6 +220,19 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kInf = __builtin_huge_valf();
 
 // ------------------------------------------------------------ decode kernel
+
+// Phase V accumulates e * v with v_dot2 over pairs of rows (one lane holds
+// the same 8 columns of rows u and u + 1 of a batch): the two rows' values
+// are interleaved into bf16 pairs with v_perm, the probabilities are rounded
+// to bf16 for the output only (scores keep fp32 probabilities), halving the
+// fp32 FMAs of the output accumulation.
+#ifndef LF_PV_DOT2
+#define LF_PV_DOT2 0
+#endif
+// Issue the first V batch before the softmax-statistics barriers.
+#ifndef LF_PREFETCH_V
+#define LF_PREFETCH_V 0
+#endif
 
 constexpr int waves_per_eu(int gp) { return gp >= 8 ? LF_WAVES_PER_EU_LARGE : LF_WAVES_PER_EU_SMALL; }
 
@@ -365,6 +406,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     }
   }
 
+  // The first V batch goes out before the softmax barriers, so the stream
+  // keeps going while the statistics are formed.
+  uint4 vbuf[U];
+  uint32_t vok = 0;
+  if (LF_PREFETCH_V && wave * ROWS < n_eff)
+    vok = load_batch<D, U, RPW>(vbuf, vrs, nvx, prev_local, mk, wave * ROWS, rg, c, n);
+
   // ---- softmax statistics of this split
   // Lanes with equal c hold the same heads; fold the row groups, then waves.
 #pragma unroll
@@ -431,43 +479,83 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   // Each row's score (single split) or |v|_1 (several splits) goes into the
   // LDS word that held the row's first logit, written by all lanes of the row
   // group (same value), and leaves for HBM in one coalesced pass afterwards.
+  auto finish_row = [&](float* slot, float vn, const float (&e)[GP], bool valid, int r) {
+    vn = allreduce_sum<LPR / 2>(vn);
+    if (SPLIT) {
+      *slot = vn;
+    } else {
+      float ps = 0.f;
+#pragma unroll
+      for (int h = 0; h < GP; ++h) ps = fmaf(e[h], il[h], ps);
+      const float sc = valid ? vn * ps : kInf;
+      const uint64_t cand = valid ? pack_candidate(sc, s0 + r) : kNoCandidate;
+      best = cand < best ? cand : best;
+      *slot = sc;
+    }
+  };
   for (int r0 = wave * ROWS; r0 < n_eff; r0 += stride) {
-    uint4 buf[U];
-    const uint32_t ok = load_batch<D, U, RPW>(buf, vrs, nvx, prev_local, mk, r0, rg, c, n);
+    if (!LF_PREFETCH_V || r0 != wave * ROWS)
+      vok = load_batch<D, U, RPW>(vbuf, vrs, nvx, prev_local, mk, r0, rg, c, n);
     float* lrow = lg + (r0 + rg) * GP;
+    if constexpr (LF_PV_DOT2) {
+      static_assert(U % 2 == 0, "rows are paired");
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool valid = (ok >> u) & 1u;
-      float vf[8];
-      bf16x8_to_f32(buf[u], vf);
-      float e[GP];
+      for (int u = 0; u < U; u += 2) {
+        const bool va = (vok >> u) & 1u, vb = (vok >> (u + 1)) & 1u;
+        float ea[GP], eb[GP];
+        uint32_t ep[GP];
 #pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        const float x = lrow[u * RPW * GP + h];  // padded: in range even past the split
-        e[h] = valid ? x : 0.f;
+        for (int h = 0; h < GP; ++h) {
+          const float xa = lrow[u * RPW * GP + h];  // padded: in range even past the split
+          const float xb = lrow[(u + 1) * RPW * GP + h];
+          ea[h] = va ? xa : 0.f;
+          eb[h] = vb ? xb : 0.f;
+          ep[h] = pack_bf16x2(ea[h], eb[h]);
+        }
+        const uint4 a = vbuf[u], bq = vbuf[u + 1];
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {bq.x, bq.y, bq.z, bq.w};
+        uint32_t vp[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vp[2 * w] = __builtin_amdgcn_perm(bw[w], aw[w], 0x05040100u);      // (a lo, b lo)
+          vp[2 * w + 1] = __builtin_amdgcn_perm(bw[w], aw[w], 0x07060302u);  // (a hi, b hi)
+        }
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            acc[h][k] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ep[h]),
+                                                        __builtin_bit_cast(bf16x2_t, vp[k]), acc[h][k], false);
+          pin8(acc[h]);
+        }
+        finish_row(lrow + u * RPW * GP, abs_sum8_bf16(a), ea, va, r0 + u * RPW + rg);
+        finish_row(lrow + (u + 1) * RPW * GP, abs_sum8_bf16(bq), eb, vb, r0 + (u + 1) * RPW + rg);
+        LF_ROW_FENCE();
       }
+    } else {
 #pragma unroll
-      for (int h = 0; h < GP; ++h) {
+      for (int u = 0; u < U; ++u) {
+        const bool valid = (vok >> u) & 1u;
+        float vf[8];
+        bf16x8_to_f32(vbuf[u], vf);
+        float e[GP];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(e[h], vf[k], acc[h][k]);
-        pin8(acc[h]);
+        for (int h = 0; h < GP; ++h) {
+          const float x = lrow[u * RPW * GP + h];  // padded: in range even past the split
+          e[h] = valid ? x : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(e[h], vf[k], acc[h][k]);
+          pin8(acc[h]);
+        }
+        float vn = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vn += fabsf(vf[k]);
+        finish_row(lrow + u * RPW * GP, vn, e, valid, r0 + u * RPW + rg);
+        LF_ROW_FENCE();
       }
-      float vn = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) vn += fabsf(vf[k]);
-      vn = allreduce_sum<LPR / 2>(vn);
-      if (SPLIT) {
-        lrow[u * RPW * GP] = vn;
-      } else {
-        float ps = 0.f;
-#pragma unroll
-        for (int h = 0; h < GP; ++h) ps = fmaf(e[h], il[h], ps);
-        const float sc = valid ? vn * ps : kInf;
-        const uint64_t cand = valid ? pack_candidate(sc, s0 + r0 + u * RPW + rg) : kNoCandidate;
-        best = cand < best ? cand : best;
-        lrow[u * RPW * GP] = sc;
-      }
-      LF_ROW_FENCE();
     }
   }
   __syncthreads();

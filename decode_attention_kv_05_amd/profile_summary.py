@@ -60,17 +60,33 @@ def _pick(means, want):
     raise KeyError(f"kernel not found among {list(means)}")
 
 
+def dispatch_durations(directory):
+    """Per-dispatch durations (ns) by kernel name, in dispatch order."""
+    out = {}
+    for row in _rows(_find(directory, "kernel_trace.csv")):
+        out.setdefault(row["Kernel_Name"], []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    return out
+
+
 def write_stats(args):
     rows = _rows(_find(args.dir, "kernel_stats.csv"))
+    try:
+        trace = dispatch_durations(args.dir)
+    except FileNotFoundError:
+        trace = {}
     out = os.path.join(PROFILES, f"longflow_decode_{args.workload}_kernels.txt")
     with open(out, "w") as f:
         f.write(f"# rocprofv3 kernel statistics, workload {args.workload}\n")
         f.write(f"# command: {args.command}\n")
         f.write(f"# kernel sources: {source_hash()}  date: {time.strftime('%Y-%m-%d')}\n")
-        f.write(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel\n")
+        f.write("# avg/min/max over every dispatch (warm-up included); p50 = median dispatch from the kernel trace\n")
+        f.write(f"{'calls':>6} {'avg_us':>10} {'p50_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel\n")
         for r in rows:
-            f.write(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
-                    f"{float(r['MaxNs']) / 1e3:>10.2f} {float(r['Percentage']):>6.2f}  {r['Name'][:110]}\n")
+            d = sorted(trace.get(r["Name"], []))
+            p50 = d[len(d) // 2] / 1e3 if d else float("nan")
+            f.write(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} {p50:>10.2f} "
+                    f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                    f"{float(r['Percentage']):>6.2f}  {r['Name'][:110]}\n")
     print(out)
 
 
