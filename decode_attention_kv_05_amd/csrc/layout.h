@@ -108,11 +108,16 @@ constexpr size_t kScratchBytes = 1024;
 // logit arrays are padded by this much so those reads need no bounds check.
 constexpr int kRowPad = 128;
 
+// LDS a workgroup may use so that two of them share a compute unit.
+constexpr size_t kHalfLdsBytes = 80 * 1024;
+
 // Wavefronts per decode workgroup for a split: a workgroup whose logits
 // leave room for a second one on the CU gets fewer waves, so that two of
 // them (which reach their barriers independently) share the CU.
 LF_HD inline int decode_waves(int gp, int split_len) {
-  return (size_t)(split_len + kRowPad) * gp * 4 > 64 * 1024 ? LF_WAVES_LARGE_LDS : LF_WAVES_SMALL_LDS;
+  return (size_t)(split_len + kRowPad) * gp * 4 + split_len + kRowPad + kScratchBytes > kHalfLdsBytes
+             ? LF_WAVES_LARGE_LDS
+             : LF_WAVES_SMALL_LDS;
 }
 
 LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len, int nw) {

@@ -72,6 +72,8 @@ int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nspli
   // trip, no combine launch); use it when there are enough pairs to give
   // every compute unit work.  Otherwise split the slots until there are
   // about two workgroups per compute unit, but not below 256 slots a split.
+  // (Smaller splits that let two workgroups share a CU measured no faster
+  // for the 16384-slot GQA-8 cache: the workspace round trip dominates.)
   if (!(need == 1 && pairs >= num_cus)) {
     const int64_t target = (2LL * num_cus + pairs - 1) / pairs;
     const int64_t cap = ((int64_t)S + 255) / 256;

@@ -10,8 +10,8 @@
 // one (sequence b, KV head j) pair.
 //
 //   setup    the split that owns prev_slot copies new_k/new_v into that cache
-//            row and reads the row from new_k/new_v for the rest of the step;
-//            the split's mask is staged in LDS.
+//            row before the workgroup barrier that follows the mask staging,
+//            so the rest of the step reads the new row from the cache.
 //   phase K  K rows stream from HBM in 16-byte lane loads (a d = 128 row is
 //            16 lanes), two batches in flight per wave.  Each lane dots its 8
 //            columns with the group's G queries; a DPP reduce-scatter over
@@ -249,20 +249,17 @@ struct Shape {
 // One batch of U rows of a cache tensor: each lane reads its 16-byte chunk
 // of rows r0 + u * RPW + rg.  Rows past the split or masked get an offset
 // outside the buffer resource and come back as zero without a memory access;
-// bit u of the result says whether row u is valid.  Row `sub_row` takes the
-// lane's chunk of the new token (`sub`) instead of the cache contents.
+// bit u of the result says whether row u is valid.
 template <int D, int U, int RPW>
 __device__ __forceinline__ uint32_t load_batch(uint4 (&buf)[U], __amdgpu_buffer_rsrc_t rows,
-                                               const uint4& sub, int sub_row,
-                                               const uint8_t* mk, int r0, int rg, int c, int n) {
+                                               const uint8_t* mk, int r0, int rg, int c) {
   uint32_t ok = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int r = r0 + u * RPW + rg;
     const bool v = mk[r] != 0;  // zero past the split
     const uint32_t off = v ? (uint32_t)r * (D * 2) + (uint32_t)c * 16 : kOutOfRange;
-    const uint4 x = load16(rows, off);
-    buf[u] = (r == sub_row) ? sub : x;
+    buf[u] = load16(rows, off);
     ok |= (uint32_t)v << u;
   }
   return ok;
@@ -326,18 +323,18 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     const uint4 x = reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G + hh) * D)[c];
     qx[h] = h < p.G ? x : make_uint4(0, 0, 0, 0);
   }
-  const uint4 nkx = reinterpret_cast<const uint4*>(nk)[c];
-  const uint4 nvx = reinterpret_cast<const uint4*>(nv)[c];
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(krows, (uint32_t)n * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vrows, (uint32_t)n * D * 2);
 
+  // The split that owns prev_slot overwrites that cache row before anything
+  // reads it: the barrier after the mask staging makes the workgroup's global
+  // writes visible to all of its threads, so the row is then streamed like any
+  // other (no other workgroup reads it during this step).
   const int prev = p.prev[pair];
-  int prev_local = -1;  // split-relative row served from new_k/new_v
   if (prev != -1) {
     if (prev < 0 || prev >= p.S) {
       if (sp == 0 && tid == 0) atomicOr(p.status, LF_DEV_BAD_PREV);
     } else if (prev >= s0 && prev < s0 + n) {
-      prev_local = prev - s0;
       if (tid < D / 8) {
         const uint4 kx = reinterpret_cast<const uint4*>(nk)[tid];
         const uint4 vx = reinterpret_cast<const uint4*>(nv)[tid];
@@ -387,7 +384,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   for (int i = 0; i < HPL; ++i) mx[i] = kNegInf;
   for (int r0 = wave * ROWS; r0 < n_eff; r0 += stride) {
     uint4 buf[U];
-    const uint32_t ok = load_batch<D, U, RPW>(buf, krs, nkx, prev_local, mk, r0, rg, c, n);
+    const uint32_t ok = load_batch<D, U, RPW>(buf, krs, mk, r0, rg, c);
     float* lrow = lg + (r0 + rg) * GP + hbase;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -411,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   uint4 vbuf[U];
   uint32_t vok = 0;
   if (LF_PREFETCH_V && wave * ROWS < n_eff)
-    vok = load_batch<D, U, RPW>(vbuf, vrs, nvx, prev_local, mk, wave * ROWS, rg, c, n);
+    vok = load_batch<D, U, RPW>(vbuf, vrs, mk, wave * ROWS, rg, c);
 
   // ---- softmax statistics of this split
   // Lanes with equal c hold the same heads; fold the row groups, then waves.
@@ -439,12 +436,16 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     const float mh = stat_m[h];
     float lsum = 0.f;
     float* wl = SPLIT ? p.ws_logit + (row0 + s0) * GP : nullptr;
-    for (int r = tid / GP; r < n_eff; r += kThreads / GP) {
+    // Rows up to the end of the last batch (all written in phase K, -inf
+    // when invalid) become e; invalid ones become exactly 0, so phase V
+    // needs no per-row select.
+    const int covered = (n_eff + ROWS - 1) / ROWS * ROWS;
+    for (int r = tid / GP; r < covered; r += kThreads / GP) {
       const float s = lg[r * GP + h];
       const float e = (s == kNegInf) ? 0.f : exp2f(s - mh);
       lg[r * GP + h] = e;
       lsum += e;
-      if (SPLIT) wl[r * GP + h] = s;
+      if (SPLIT && r < n_eff) wl[r * GP + h] = s;
     }
 #pragma unroll
     for (int m = GP; m < 64; m <<= 1) lsum += __shfl_xor(lsum, m);
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   };
   for (int r0 = wave * ROWS; r0 < n_eff; r0 += stride) {
     if (!LF_PREFETCH_V || r0 != wave * ROWS)
-      vok = load_batch<D, U, RPW>(vbuf, vrs, nvx, prev_local, mk, r0, rg, c, n);
+      vok = load_batch<D, U, RPW>(vbuf, vrs, mk, r0, rg, c);
     float* lrow = lg + (r0 + rg) * GP;
     if constexpr (LF_PV_DOT2) {
       static_assert(U % 2 == 0, "rows are paired");
@@ -538,12 +539,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
         const bool valid = (vok >> u) & 1u;
         float vf[8];
         bf16x8_to_f32(vbuf[u], vf);
-        float e[GP];
+        float e[GP];  // exactly 0 for invalid rows (see the softmax pass)
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-          const float x = lrow[u * RPW * GP + h];  // padded: in range even past the split
-          e[h] = valid ? x : 0.f;
-        }
+        for (int h = 0; h < GP; ++h) e[h] = lrow[u * RPW * GP + h];
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
 #pragma unroll
