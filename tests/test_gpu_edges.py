@@ -1,0 +1,108 @@
+"""Edge cases of the C ABI on the GPU: the auto-planned entry point called
+directly, the largest single-split slot counts the LDS allows for every group
+size, and a seeded sweep of random shapes, split counts and masks, each
+against the fp64 oracle (same acceptance as tests/test_gpu_parity.py)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_05_amd import workloads as W
+from gpu_util import Lockstep, bf16_dev, bf16_host, bf16_value, compare_pair, log
+from oracle import decode_step
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    yield
+
+
+def _largest_single_split(lf, G, d):
+    """Largest S for which one split per pair passes validation (host only)."""
+    lo, hi = 1, 1 << 17
+    base = 1 << 40
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        ws = lf.lf_workspace_size(1, G, 1, d, mid, 1)
+        a = [base + i * (1 << 34) for i in range(11)]
+        rc = lf.lf_validate(1, G, 1, d, mid, 0.1, *a, ws, 1)
+        lo, hi = (mid, hi) if rc == lf.LF_OK else (lo, mid - 1)
+    return lo
+
+
+def test_auto_entry_point_matches_explicit_plan():
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("auto", B=3, Hq=16, Hkv=4, d=128, S=1500, steps=1, kind="ragged", seed=9100, len_lo=100)
+    k, v, mask = W.initial_cache(wl)
+    q, nk, nv = W.step_inputs(wl, 0)
+    assert lf.lf_device_num_cus() > 0
+    ns = lf.plan_nsplit(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S)
+    ws_bytes = lf.lf_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, ns)
+    results = []
+    for use_auto in (True, False):
+        dk, dv = bf16_dev(k), bf16_dev(v)
+        dq, dnk, dnv = bf16_dev(q), bf16_dev(nk), bf16_dev(nv)
+        dm = torch.from_numpy(mask).cuda()
+        prev = torch.full((wl.B, wl.Hkv), 3, dtype=torch.int32, device="cuda")
+        out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device="cuda")
+        sc = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device="cuda")
+        ev = torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device="cuda")
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        args = [wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, float(wl.scale), P(dq), P(dk), P(dv), P(dm), P(dnk), P(dnv),
+                P(prev), P(out), P(sc), P(ev), P(ws), ws_bytes]
+        if use_auto:
+            rc = lf._lib.longflow_decode(*args, stream)
+        else:
+            rc = lf._lib.longflow_decode_nsplit(*args, ns, stream)
+        assert rc == 0, lf.lf_strerror(rc)
+        torch.cuda.synchronize()
+        results.append((bf16_host(out), sc.cpu().numpy(), ev.cpu().numpy(), bf16_host(dk)))
+    for a, b in zip(*results):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_largest_single_split(G, d):
+    """One workgroup holding the most slots the LDS allows (close to the
+    160 KB of a compute unit), against the oracle, two steps."""
+    from decode_attention_kv_05_amd import longflow as lf
+    S = _largest_single_split(lf, G, d)
+    assert lf.lf_validate(1, G, 1, d, S + 64, 0.1, *[(1 << 40) + i * (1 << 34) for i in range(11)],
+                          lf.lf_workspace_size(1, G, 1, d, S + 64, 1), 1) == lf.LF_E_NSPLIT
+    wl = W.Workload(f"max_g{G}_d{d}", B=1, Hq=G, Hkv=1, d=d, S=S, steps=2, kind="plain", seed=9200 + G,
+                    valid=S - 7)
+    log(f"largest single split G={G} d={d} S={S}")
+    ls = Lockstep(wl, nsplit=1)
+    for _ in range(wl.steps):
+        ls.step()
+    ls.check_full_cache()
+
+
+def test_random_shapes_sweep():
+    """Seeded random shapes, masks and split counts (including one slot per
+    split), three lockstep steps each."""
+    rng = np.random.default_rng(20261202)
+    for case in range(12):
+        G = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        Hkv = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        S = int(rng.integers(1, 700))
+        B = int(rng.integers(1, 4))
+        kind = str(rng.choice(["plain", "ragged", "sinks", "lognormal_v"]))
+        wl = W.Workload(f"rand{case}", B=B, Hq=G * Hkv, Hkv=Hkv, d=d, S=S, steps=3, kind=kind,
+                        seed=9300 + case, len_lo=1, valid=0 if kind != "plain" else int(rng.integers(0, S + 1)))
+        nsplit = int(rng.choice([1, 2, 5, S]))
+        log(f"case {case}: {wl} nsplit={nsplit}")
+        ls = Lockstep(wl, nsplit=nsplit)
+        for _ in range(wl.steps):
+            ls.step()
+        ls.check_full_cache()
