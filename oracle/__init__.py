@@ -4,6 +4,7 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
 package; the library never imports it.
 """
 
-from .longflow_oracle import attend_pair, bf16_bits_to_f64, decode_step, write_slot
+from .longflow_oracle import (attend_pair, bf16_bits_to_f64, decode_step, decode_step_fill, evict_topk,
+                              write_slot)
 
-__all__ = ["attend_pair", "bf16_bits_to_f64", "decode_step", "write_slot"]
+__all__ = ["attend_pair", "bf16_bits_to_f64", "decode_step", "decode_step_fill", "evict_topk", "write_slot"]

@@ -166,3 +166,80 @@ def decode_step(q_bits, k_bits, v_bits, mask, new_k_bits, new_v_bits, prev_slot,
         scores[b, j] = s_j
         evict[b, j] = e_j
     return out, scores, evict
+
+
+def decode_step_fill(q_bits, k_bits, v_bits, mask_in, new_k_bits, new_v_bits, prev_slot, scale):
+    """One decode step over a static cache that may still have free slots.
+
+    The cache lifecycle of Figure 2 (Left panel), read with its mask: slots
+    whose mask bit is 0 are free.  The current token is written into
+    prev_slot as in decode_step, and that slot counts as valid for the same
+    step whether or not its mask bit was set.  The returned mask_out is
+    mask_in with every written slot set.  The slot for the next token is the
+    lowest free slot of mask_out when the sequence still has one (the cache
+    fills up before anything is evicted); once the cache is full it is the
+    evicted slot of decode_step.  Every KV head of a sequence writes the
+    same slot while the sequence is filling, so mask_out is well defined.
+
+    Returns (O float64 [B,Hq,d], scores float64 [B,Hkv,S], next_slot int32
+    [B,Hkv], mask_out uint8 [B,S]); k_bits/v_bits are updated in place.
+    """
+    B, Hq, d = q_bits.shape
+    _, Hkv, S, _ = k_bits.shape
+    gsize = Hq // Hkv
+    mask_in = np.asarray(mask_in)
+    mask_out = (mask_in != 0).astype(np.uint8)
+    out = np.zeros((B, Hq, d))
+    scores = np.full((B, Hkv, S), np.inf)
+    nxt = np.full((B, Hkv), -1, dtype=np.int32)
+    for b in range(B):
+        for j in range(Hkv):
+            written = write_slot(k_bits[b, j], v_bits[b, j], new_k_bits[b, j], new_v_bits[b, j],
+                                 prev_slot[b, j])
+            valid = mask_in[b] != 0
+            if written:
+                valid = valid.copy()
+                valid[int(prev_slot[b, j])] = True
+                mask_out[b, int(prev_slot[b, j])] = 1
+            heads = slice(j * gsize, (j + 1) * gsize)
+            k = np.zeros((S, d))
+            v = np.zeros((S, d))
+            k[valid] = bf16_bits_to_f64(k_bits[b, j][valid])
+            v[valid] = bf16_bits_to_f64(v_bits[b, j][valid])
+            o_j, s_j, e_j = attend_pair(bf16_bits_to_f64(q_bits[b, heads]), k, v, valid, float(scale))
+            out[b, heads] = o_j
+            scores[b, j] = s_j
+            nxt[b, j] = e_j
+    for b in range(B):
+        free = np.flatnonzero(mask_out[b] == 0)
+        if free.size:
+            nxt[b, :] = free[0]
+    return out, scores, nxt, mask_out
+
+
+def evict_topk(scores, valid, k):
+    """Several slots evicted at once (periodic compression): the set of the k
+    valid slots that come first in (score, slot) order, listed in ascending
+    slot order and padded with -1 when fewer than k slots are valid.  With
+    k = 1 this is decode_step's eviction rule.
+
+    Scores compare by value (so -0 equals +0 and the slot decides); NaN
+    scores come after every number, +inf included.
+
+    scores: [..., S] float; valid: [..., S] bool; returns int32 [..., k].
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    valid = np.asarray(valid, dtype=bool)
+    lead = scores.shape[:-1]
+    S = scores.shape[-1]
+    flat_s = scores.reshape(-1, S)
+    flat_v = np.broadcast_to(valid, scores.shape).reshape(-1, S)
+    out = np.full((flat_s.shape[0], k), -1, dtype=np.int32)
+    for r in range(flat_s.shape[0]):
+        idx = np.flatnonzero(flat_v[r])
+        # (score, slot) order: a stable sort of the ascending slots by score;
+        # numpy's sort places NaN after every number.
+        order = idx[np.argsort(flat_s[r, idx], kind="stable")]
+        take = np.sort(order[:k])
+        out[r, :take.size] = take
+    return out.reshape(*lead, k)
