@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblongflow.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "longflow_api.cpp"), os.path.join(CSRC, "longflow_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "longflow_api.cpp"), os.path.join(CSRC, "longflow_kernels.hip"),
+           os.path.join(CSRC, "evict_topk.hip")]
 ARCH = "gfx950"
 
 

@@ -24,12 +24,23 @@ struct DecodeParams {
   float* ws_logit;        // workspace: [pairs][S][GP]
   float* ws_vnorm;        // workspace: [pairs][S]
   uint64_t* cand;         // workspace: [pairs][chunks] packed (score, slot) minima
+  uint32_t* ffree;        // workspace: [pairs][chunks] lowest free slot (fill step)
+  uint8_t* mask_w;        // fill step: the same mask, updated in place; else null
   int Hq, Hkv, G, S, nsplit, split_len;
+  int fill;               // 1: fill step (next slot = lowest free slot while any)
   float qscale;           // logit scale times log2(e)
+};
+
+struct TopkParams {
+  const float* scores;    // [B][Hkv][S]
+  const uint8_t* mask;    // [B][S]
+  int32_t* out;           // [k][B][Hkv]
+  int Hkv, S, k, pairs;
 };
 
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
                          hipStream_t stream);
+hipError_t launch_topk(const TopkParams& prm, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 
 }  // namespace lf

@@ -65,6 +65,7 @@ struct WorkspaceLayout {
   size_t logit;     // float [pairs][S][GP]: log2-domain logits
   size_t vnorm;     // float [pairs][S]: |v|_1 per slot
   size_t cand;      // uint64 [pairs][combine chunks]: per-chunk (score, slot) minima
+  size_t ffree;     // uint32 [pairs][combine chunks]: per-chunk lowest free slot (fill step)
   size_t total;
 };
 
@@ -88,8 +89,10 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
     off = align_up(off + pairs * (size_t)S * 4, 256);
     w.cand = off;
     off = align_up(off + pairs * (size_t)combine_chunks(S) * 8, 256);
+    w.ffree = off;
+    off = align_up(off + pairs * (size_t)combine_chunks(S) * 4, 256);
   } else {
-    w.part_ml = w.part_o = w.logit = w.vnorm = w.cand = off;
+    w.part_ml = w.part_o = w.logit = w.vnorm = w.cand = w.ffree = off;
   }
   w.total = off;
   return w;

@@ -128,11 +128,17 @@ int lf_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
              : LF_E_HIP;
 }
 
-int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
-                const void* k_cache, const void* v_cache, const uint8_t* mask, const void* new_k,
-                const void* new_v, const int32_t* prev_slot, const void* out, const float* scores,
-                const int32_t* evict_slot, const void* workspace, size_t workspace_bytes,
-                int nsplit) {
+}  // extern "C"
+
+namespace {
+
+// The checks of lf_validate; `mask_written` marks the fill step, which
+// updates the mask in place (so it must not overlap any other buffer).
+int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                  const void* k_cache, const void* v_cache, const uint8_t* mask, const void* new_k,
+                  const void* new_v, const int32_t* prev_slot, const void* out, const float* scores,
+                  const int32_t* evict_slot, const void* workspace, size_t workspace_bytes,
+                  int nsplit, bool mask_written) {
   int rc = lf_check_shape(B, Hq, Hkv, d, S);
   if (rc != LF_OK) return rc;
   if (!std::isfinite(scale)) return LF_E_VALUE;
@@ -167,7 +173,7 @@ int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale, const void* q
     bool written;
   };
   const Buf bufs[] = {
-      {q, q_bytes, false},           {mask, mask_bytes, false},   {new_k, row_bytes, false},
+      {q, q_bytes, false},           {mask, mask_bytes, mask_written}, {new_k, row_bytes, false},
       {new_v, row_bytes, false},     {prev_slot, idx_bytes, false}, {k_cache, cache_bytes, true},
       {v_cache, cache_bytes, true},  {out, q_bytes, true},        {scores, score_bytes, true},
       {evict_slot, idx_bytes, true}, {workspace, ws_need, true},
@@ -182,16 +188,12 @@ int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale, const void* q
   return LF_OK;
 }
 
-int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
-                           void* k_cache, void* v_cache, const uint8_t* mask, const void* new_k,
-                           const void* new_v, const int32_t* prev_slot, void* out, float* scores,
-                           int32_t* evict_slot, void* workspace, size_t workspace_bytes,
-                           int nsplit, void* stream) {
-  int rc = lf_validate(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v,
-                       prev_slot, out, scores, evict_slot, workspace, workspace_bytes, nsplit);
-  if (rc != LF_OK) return rc;
-  if (B == 0) return LF_OK;
-
+// Enqueue one step after validation: the decode kernel, and for several
+// splits the combine and finalize kernels.
+int enqueue_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q, void* k_cache,
+                 void* v_cache, const uint8_t* mask, uint8_t* mask_w, const void* new_k,
+                 const void* new_v, const int32_t* prev_slot, void* out, float* scores,
+                 int32_t* evict_slot, void* workspace, int nsplit, void* stream) {
   const int G = Hq / Hkv;
   const int gp = lf::padded_group(G);
   int len, eff;
@@ -204,6 +206,8 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
   prm.k = static_cast<uint16_t*>(k_cache);
   prm.v = static_cast<uint16_t*>(v_cache);
   prm.mask = mask;
+  prm.mask_w = mask_w;
+  prm.fill = mask_w != nullptr;
   prm.new_k = static_cast<const uint16_t*>(new_k);
   prm.new_v = static_cast<const uint16_t*>(new_v);
   prm.prev = prev_slot;
@@ -216,6 +220,7 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
   prm.ws_logit = reinterpret_cast<float*>(ws + wl.logit);
   prm.ws_vnorm = reinterpret_cast<float*>(ws + wl.vnorm);
   prm.cand = reinterpret_cast<uint64_t*>(ws + wl.cand);
+  prm.ffree = reinterpret_cast<uint32_t*>(ws + wl.ffree);
   prm.Hq = Hq;
   prm.Hkv = Hkv;
   prm.G = G;
@@ -234,6 +239,32 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
              : LF_E_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                const void* k_cache, const void* v_cache, const uint8_t* mask, const void* new_k,
+                const void* new_v, const int32_t* prev_slot, const void* out, const float* scores,
+                const int32_t* evict_slot, const void* workspace, size_t workspace_bytes,
+                int nsplit) {
+  return validate_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v, prev_slot,
+                       out, scores, evict_slot, workspace, workspace_bytes, nsplit, false);
+}
+
+int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                           void* k_cache, void* v_cache, const uint8_t* mask, const void* new_k,
+                           const void* new_v, const int32_t* prev_slot, void* out, float* scores,
+                           int32_t* evict_slot, void* workspace, size_t workspace_bytes,
+                           int nsplit, void* stream) {
+  int rc = lf_validate(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v,
+                       prev_slot, out, scores, evict_slot, workspace, workspace_bytes, nsplit);
+  if (rc != LF_OK) return rc;
+  if (B == 0) return LF_OK;
+  return enqueue_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, nullptr, new_k, new_v,
+                      prev_slot, out, scores, evict_slot, workspace, nsplit, stream);
+}
+
 int longflow_decode(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
                     void* k_cache, void* v_cache, const uint8_t* mask, const void* new_k,
                     const void* new_v, const int32_t* prev_slot, void* out, float* scores,
@@ -250,6 +281,52 @@ int longflow_decode(int B, int Hq, int Hkv, int d, int S, float scale, const voi
   return longflow_decode_nsplit(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v,
                                 prev_slot, out, scores, evict_slot, workspace, workspace_bytes,
                                 nsplit, stream);
+}
+
+int longflow_decode_fill(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                         void* k_cache, void* v_cache, uint8_t* mask, const void* new_k,
+                         const void* new_v, const int32_t* prev_slot, void* out, float* scores,
+                         int32_t* next_slot, void* workspace, size_t workspace_bytes, int nsplit,
+                         void* stream) {
+  int rc = lf_check_shape(B, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  if (nsplit < 0) return LF_E_NSPLIT;
+  if (B == 0) return std::isfinite(scale) ? LF_OK : LF_E_VALUE;
+  if (nsplit == 0) {
+    int cus = 0;
+    rc = lf_device_num_cus(&cus);
+    if (rc != LF_OK) return rc;
+    rc = lf_plan_nsplit(B, Hq, Hkv, d, S, cus, &nsplit);
+    if (rc != LF_OK) return rc;
+  }
+  rc = validate_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v, prev_slot,
+                     out, scores, next_slot, workspace, workspace_bytes, nsplit, true);
+  if (rc != LF_OK) return rc;
+  return enqueue_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, mask, new_k, new_v,
+                      prev_slot, out, scores, next_slot, workspace, nsplit, stream);
+}
+
+int longflow_evict_topk(int B, int Hkv, int S, int k, const float* scores, const uint8_t* mask,
+                        int32_t* evict_slots, void* stream) {
+  if (B < 0 || Hkv < 1 || S < 1 || k < 1 || k > S) return LF_E_SHAPE;
+  if ((int64_t)B * Hkv > INT_MAX || (int64_t)B * Hkv * k > INT_MAX) return LF_E_SHAPE;
+  if (B == 0) return LF_OK;
+  if (!scores || !mask || !evict_slots) return LF_E_NULL;
+  if (misaligned(scores, 4) || misaligned(evict_slots, 4)) return LF_E_ALIGN;
+  const size_t pairs = (size_t)B * Hkv;
+  const size_t out_bytes = pairs * k * 4;
+  if (overlaps(evict_slots, out_bytes, scores, pairs * S * 4) ||
+      overlaps(evict_slots, out_bytes, mask, (size_t)B * S))
+    return LF_E_ALIAS;
+  lf::TopkParams prm{};
+  prm.scores = scores;
+  prm.mask = mask;
+  prm.out = evict_slots;
+  prm.Hkv = Hkv;
+  prm.S = S;
+  prm.k = k;
+  prm.pairs = (int)pairs;
+  return lf::launch_topk(prm, static_cast<hipStream_t>(stream)) == hipSuccess ? LF_OK : LF_E_HIP;
 }
 
 int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags) {

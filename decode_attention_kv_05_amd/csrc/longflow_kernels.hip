@@ -38,6 +38,7 @@
 // decides exact ties.
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -304,6 +305,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   float* stat_il = stat_m + GP;                                  // [GP] 1 / L
   uint64_t* best_w = reinterpret_cast<uint64_t*>(stat_il + GP);  // [NW]
   int* red_i = reinterpret_cast<int*>(best_w + NW);              // [NW]
+  int* red_f = red_i + NW;                                       // [NW] fill step
 
   const size_t row0 = (size_t)pair * p.S;  // first cache row of this pair
   const uint16_t* krows = p.k + (row0 + s0) * D;
@@ -341,12 +343,29 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
         reinterpret_cast<uint4*>(p.k + (row0 + prev) * D)[tid] = kx;
         reinterpret_cast<uint4*>(p.v + (row0 + prev) * D)[tid] = vx;
       }
-      if (tid == 0 && mrow[prev] == 0) atomicOr(p.status, LF_DEV_WRITE_MASKED);
+      if (tid == 0 && mrow[prev] == 0) {
+        if (p.fill) {
+          // A free slot: it joins the mask.  The mask is shared by the KV
+          // heads, so all of them must be writing this same slot.
+          p.mask_w[(size_t)b * p.S + prev] = 1;
+          for (int jj = 0; jj < p.Hkv; ++jj)
+            if (p.prev[(size_t)b * p.Hkv + jj] != prev) {
+              atomicOr(p.status, LF_DEV_FILL_DIVERGED);
+              break;
+            }
+        } else {
+          atomicOr(p.status, LF_DEV_WRITE_MASKED);
+        }
+      }
     }
   }
   // Mask of the split into LDS, zero-padded past its end; n_eff = one past
-  // the last valid row, so trailing masked rows are never streamed.
+  // the last valid row, so trailing masked rows are never streamed.  A fill
+  // step also counts the slot it wrote as valid (whatever the mask byte
+  // reads while other workgroups update it) and finds the lowest free slot.
   int last_valid = -1;
+  int first_free = INT_MAX;
+  const int own = (p.fill && prev >= s0 && prev < s0 + n) ? prev - s0 : -1;
   {
     const uint8_t* src = mrow + s0;
     const int npad = n + kRowPad;
@@ -355,18 +374,24 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = base + u * kThreads + tid;
-        t8[u] = i < n ? src[i] : 0;
+        t8[u] = i < n ? (uint8_t)(src[i] | (i == own)) : 0;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = base + u * kThreads + tid;
         if (i < npad) mk[i] = t8[u];
         if (t8[u] != 0) last_valid = i;
+        if (!SPLIT && i < n && t8[u] == 0) first_free = min(first_free, i);
       }
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) last_valid = max(last_valid, __shfl_xor(last_valid, m));
     if (lane == 0) red_i[wave] = last_valid;
+    if (!SPLIT && p.fill) {
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) first_free = min(first_free, __shfl_xor(first_free, m));
+      if (lane == 0) red_f[wave] = first_free;
+    }
   }
   __syncthreads();
   int n_eff = 0;
@@ -599,7 +624,15 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
       uint64_t m = best_w[0];
 #pragma unroll
       for (int w = 1; w < NW; ++w) m = best_w[w] < m ? best_w[w] : m;
-      p.evict[pair] = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
+      int32_t next = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
+      if (p.fill) {
+        // while the sequence has a free slot, the next token goes there
+        int ff = INT_MAX;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) ff = min(ff, red_f[w]);
+        if (ff != INT_MAX) next = ff;
+      }
+      p.evict[pair] = next;
     }
   } else {
     float* po = p.part_o + ((size_t)pair * nsplit + sp) * GP * D;
@@ -633,6 +666,7 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
   constexpr int R = kCombineRowsPerThread;
   __shared__ float stat_m[GP], stat_il[GP];
   __shared__ uint64_t best_w[NWC];
+  __shared__ int free_w[NWC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -716,6 +750,19 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
       for (int h = 0; h < GP; ++h) s[u][h] = valid[u] ? wl[(size_t)r * GP + h] : 0.f;
     }
   }
+  // Fill step: the lowest free slot of the chunk.  The decode kernel has
+  // already added the written slots to the mask.
+  if (p.fill) {
+    int ff = INT_MAX;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int r = base + u * kCombineThreads + tid;
+      if (r < p.S && !valid[u]) ff = min(ff, r);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) ff = min(ff, __shfl_xor(ff, m));
+    if (lane == 0) free_w[wave] = ff;
+  }
   uint64_t best = kNoCandidate;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
@@ -739,6 +786,12 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
 #pragma unroll
     for (int w = 1; w < NWC; ++w) m = best_w[w] < m ? best_w[w] : m;
     p.cand[(size_t)pair * nchunk + chunk] = m;
+    if (p.fill) {
+      int ff = free_w[0];
+#pragma unroll
+      for (int w = 1; w < NWC; ++w) ff = min(ff, free_w[w]);
+      p.ffree[(size_t)pair * nchunk + chunk] = (uint32_t)ff;
+    }
   }
 }
 
@@ -748,7 +801,13 @@ __global__ void longflow_finalize_kernel(DecodeParams p, int pairs, int nchunk) 
   const uint64_t* c = p.cand + (size_t)pair * nchunk;
   uint64_t m = kNoCandidate;
   for (int i = 0; i < nchunk; ++i) m = c[i] < m ? c[i] : m;
-  p.evict[pair] = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
+  int32_t next = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
+  if (p.fill) {
+    uint32_t ff = (uint32_t)INT_MAX;
+    for (int i = 0; i < nchunk; ++i) ff = min(ff, p.ffree[(size_t)pair * nchunk + i]);
+    if (ff != (uint32_t)INT_MAX) next = (int32_t)ff;
+  }
+  p.evict[pair] = next;
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {

@@ -25,11 +25,12 @@ LF_E_VALUE = -8
 
 LF_DEV_BAD_PREV = 0x1
 LF_DEV_WRITE_MASKED = 0x2
+LF_DEV_FILL_DIVERGED = 0x4
 
 EXPORTED = (
     "lf_version", "lf_strerror", "lf_check_shape", "lf_plan_nsplit", "lf_workspace_size",
     "lf_device_num_cus", "lf_workspace_init", "lf_validate", "longflow_decode",
-    "longflow_decode_nsplit", "lf_read_device_status",
+    "longflow_decode_nsplit", "longflow_decode_fill", "longflow_evict_topk", "lf_read_device_status",
 )
 
 _i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -50,6 +51,8 @@ def _load():
         "lf_validate": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i], _i),
         "longflow_decode": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _p], _i),
         "longflow_decode_nsplit": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i, _p], _i),
+        "longflow_decode_fill": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i, _p], _i),
+        "longflow_evict_topk": ([_i] * 4 + [_p] * 3 + [_p], _i),
         "lf_read_device_status": ([_p, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
     }
     for name, (args, res) in sig.items():
@@ -149,19 +152,8 @@ def _need(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
-                    out=None, scores=None, evict_slot=None, workspace=None, nsplit=None,
-                    stream=None):
-    """One fused decode step; returns (out, scores, evict_slot).
-
-    q [B, Hq, d] bf16; k_cache, v_cache [B, Hkv, S, d] bf16 (updated in place);
-    mask [B, S] uint8 or bool; new_k, new_v [B, Hkv, d] bf16; prev_slot
-    [B, Hkv] int32.  Outputs are allocated when not given: out [B, Hq, d]
-    bf16, scores [B, Hkv, S] float32, evict_slot [B, Hkv] int32.  scale
-    defaults to 1/sqrt(d).  nsplit None uses the library's plan for the
-    device.  The work is enqueued on `stream` (default: torch's current
-    stream) and not waited for.
-    """
+def _step(entry, q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out, scores, evict_slot,
+          workspace, nsplit, stream):
     B, Hq, d = q.shape
     Hkv, S = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
@@ -190,13 +182,61 @@ def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the device of q")
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
-    rc = _lib.longflow_decode_nsplit(
+    rc = getattr(_lib, entry)(
         B, Hq, Hkv, d, S, float(scale), ptr(q), ptr(k_cache), ptr(v_cache), ptr(mask),
         ptr(new_k), ptr(new_v), ptr(prev_slot), ptr(out), ptr(scores), ptr(evict_slot),
         ptr(workspace), workspace.numel() * workspace.element_size(), int(nsplit),
         _stream_ptr(stream, dev))
-    _check(rc, "longflow_decode")
+    _check(rc, entry)
     return out, scores, evict_slot
+
+
+def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
+                    out=None, scores=None, evict_slot=None, workspace=None, nsplit=None,
+                    stream=None):
+    """One fused decode step; returns (out, scores, evict_slot).
+
+    q [B, Hq, d] bf16; k_cache, v_cache [B, Hkv, S, d] bf16 (updated in place);
+    mask [B, S] uint8 or bool; new_k, new_v [B, Hkv, d] bf16; prev_slot
+    [B, Hkv] int32.  Outputs are allocated when not given: out [B, Hq, d]
+    bf16, scores [B, Hkv, S] float32, evict_slot [B, Hkv] int32.  scale
+    defaults to 1/sqrt(d).  nsplit None uses the library's plan for the
+    device.  The work is enqueued on `stream` (default: torch's current
+    stream) and not waited for.
+    """
+    return _step("longflow_decode_nsplit", q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
+                 scores, evict_slot, workspace, nsplit, stream)
+
+
+def longflow_decode_fill(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
+                         out=None, scores=None, next_slot=None, workspace=None, nsplit=None,
+                         stream=None):
+    """One decode step of the fill phase; returns (out, scores, next_slot).
+
+    As longflow_decode, except that `mask` is updated in place (the written
+    slot becomes valid) and next_slot is the lowest free slot of the updated
+    mask while the sequence has one, else the evicted slot.
+    """
+    return _step("longflow_decode_fill", q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
+                 scores, next_slot, workspace, nsplit, stream)
+
+
+def longflow_evict_topk(scores, mask, k, *, out=None, stream=None):
+    """The k valid slots first in (score, slot) order for every (b, j), in
+    ascending slot order, -1 padded: int32 [k, B, Hkv] (entry t is a
+    prev_slot array for the t-th following step)."""
+    B, Hkv, S = scores.shape
+    dev = scores.device
+    _need(scores, "scores", torch.float32, (B, Hkv, S), dev)
+    _need(mask, "mask", (torch.uint8, torch.bool), (B, S), dev)
+    if out is None:
+        out = torch.empty((k, B, Hkv), dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, (k, B, Hkv), dev)
+    rc = _lib.longflow_evict_topk(B, Hkv, S, int(k), ctypes.c_void_p(scores.data_ptr()),
+                                  ctypes.c_void_p(mask.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  _stream_ptr(stream, dev))
+    _check(rc, "longflow_evict_topk")
+    return out
 
 
 def lf_read_device_status(workspace, stream=None):

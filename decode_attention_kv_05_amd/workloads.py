@@ -27,7 +27,7 @@ import numpy as np
 BF16_NAN = 0x7FC0
 
 # Purpose codes of the keyed streams.
-_K, _V, _Q, _NEWK, _NEWV, _DIR, _PLANT, _TWIN, _LEN, _VNORM, _NEWVNORM = range(1, 12)
+_K, _V, _Q, _NEWK, _NEWV, _DIR, _PLANT, _TWIN, _LEN, _VNORM, _NEWVNORM, _HOLES, _SCORES = range(1, 14)
 
 KINDS = ("plain", "sinks", "lognormal_v", "ragged")
 
@@ -226,3 +226,48 @@ def first_prev_slot(wl, batch=None):
     """prev_slot of step 0: -1 everywhere (no slot was chosen before the first step)."""
     return np.full((len(_batch_list(wl, batch)), wl.Hkv), -1, dtype=np.int32)
 
+
+
+def holed_mask(wl, frac_valid, batch=None):
+    """uint8 [nb, S]: each slot valid with probability frac_valid, drawn per
+    sequence (free slots scattered through the cache)."""
+    bl = _batch_list(wl, batch)
+    m = np.zeros((len(bl), wl.S), dtype=np.uint8)
+    for r, b in enumerate(bl):
+        m[r] = _rng(wl, _HOLES, 0, b).random(wl.S) < frac_valid
+    return m
+
+
+def poison_free(k, v, mask):
+    """Fill the K/V rows of every slot whose mask byte is 0 with a bf16 NaN."""
+    free = mask == 0
+    for j in range(k.shape[1]):
+        k[:, j][free] = BF16_NAN
+        v[:, j][free] = BF16_NAN
+
+
+def synthetic_scores(B, Hkv, S, seed, kind="ties"):
+    """float32 [B, Hkv, S] stand-ins for the operator's scores, for testing
+    slot selection on its own.  Drawn per sequence b.
+      ties     multiples of 1/8 in [0, 2): many exact ties
+      spread   log-normal values, distinct almost surely
+      special  ties plus about 2% each of +0/-0, +inf, NaN and negative values
+    """
+    out = np.empty((B, Hkv, S), dtype=np.float32)
+    for b in range(B):
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _SCORES, 0, b])))
+        if kind == "spread":
+            out[b] = np.exp(g.standard_normal((Hkv, S))).astype(np.float32)
+            continue
+        x = (g.integers(0, 16, size=(Hkv, S)) / 8.0).astype(np.float32)
+        if kind == "special":
+            u = g.random((Hkv, S))
+            x[u < 0.02] = np.float32(0.0)
+            x[(u >= 0.02) & (u < 0.04)] = np.float32(-0.0)
+            x[(u >= 0.04) & (u < 0.06)] = np.float32(np.inf)
+            x[(u >= 0.06) & (u < 0.08)] = np.float32(np.nan)
+            x[(u >= 0.08) & (u < 0.10)] *= np.float32(-1.0)
+        elif kind != "ties":
+            raise ValueError(f"unknown score kind {kind!r}")
+        out[b] = x
+    return out

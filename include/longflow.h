@@ -90,6 +90,8 @@ typedef enum lf_status {
 /* Device status bits, accumulated in the workspace across calls until cleared. */
 #define LF_DEV_BAD_PREV 0x1u     /* prev_slot outside {-1} U [0, S): write skipped */
 #define LF_DEV_WRITE_MASKED 0x2u /* prev_slot named a masked slot: written, unused */
+#define LF_DEV_FILL_DIVERGED 0x4u /* fill step: the KV heads of a sequence did not all
+                                     write the same free slot (see longflow_decode_fill) */
 
 /* ABI version (LF_ABI_VERSION). */
 int lf_version(void);
@@ -145,6 +147,53 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale,
                            const int32_t* prev_slot, void* out, float* scores,
                            int32_t* evict_slot, void* workspace, size_t workspace_bytes,
                            int nsplit, void* stream);
+
+/* One decode step of the cache's fill phase: the static cache still has free
+ * slots (mask 0), which are used up before anything is evicted.  Same
+ * arguments, shapes and workspace as longflow_decode_nsplit, except:
+ *   mask       uint8 [B][S]   read and updated in place: the slot written for
+ *                             a sequence becomes valid (mask 1)
+ *   next_slot  int32 [B][Hkv] the slot for the next step's token: the lowest
+ *                             free slot of the updated mask while the
+ *                             sequence has one, otherwise the evicted slot
+ *                             of longflow_decode
+ *   nsplit     0 = the count lf_plan_nsplit chooses for the current device
+ * The written slot takes part in the same step's attention whether or not it
+ * was free (Figure 2, Left panel: the current token is written, then
+ * attended), so a sequence that starts empty with prev_slot = 0 gets plain
+ * causal decode attention until its cache is full; after that the step is
+ * exactly longflow_decode.  Writing a free slot sets no LF_DEV_WRITE_MASKED.
+ * The mask is shared by the KV heads, so while a sequence has free slots all
+ * of its KV heads must write the same slot (or none); otherwise
+ * LF_DEV_FILL_DIVERGED is set and that sequence's results are unspecified
+ * (every access stays in bounds).  The next_slot values this entry point
+ * returns always satisfy that rule. */
+int longflow_decode_fill(int B, int Hq, int Hkv, int d, int S, float scale,
+                         const void* q, void* k_cache, void* v_cache, uint8_t* mask,
+                         const void* new_k, const void* new_v, const int32_t* prev_slot,
+                         void* out, float* scores, int32_t* next_slot, void* workspace,
+                         size_t workspace_bytes, int nsplit, void* stream);
+
+/* Several slots evicted at once, for a periodic cadence (compress every N
+ * steps instead of every step).  For every (b, j): the set of the k valid
+ * slots (mask[b][i] != 0) that come first in (score, slot) order, written in
+ * ascending slot order; when fewer than k slots are valid the set is all of
+ * them and the rest of the list is -1.  Scores compare by value (-0 equals
+ * +0, so the slot decides) and NaN comes after every number; with k = 1 this
+ * is longflow_decode's eviction rule.
+ *   scores       fp32  [B][Hkv][S]  read (typically longflow_decode's output)
+ *   mask         uint8 [B][S]       read
+ *   evict_slots  int32 [k][B][Hkv]  written; entry t is laid out like a
+ *                                   prev_slot array, so `evict_slots + t*B*Hkv`
+ *                                   can be passed as prev_slot of the t-th
+ *                                   following step (a write queue: the listed
+ *                                   slots stay valid and are attended until
+ *                                   their turn to be overwritten comes)
+ * Sizes: B >= 0 (0 = no-op), Hkv >= 1, S >= 1, 1 <= k <= S.  Alignment:
+ * scores and evict_slots on 4 bytes.  evict_slots must not overlap scores or
+ * mask.  Asynchronous on `stream`, no workspace, no allocation. */
+int longflow_evict_topk(int B, int Hkv, int S, int k, const float* scores,
+                        const uint8_t* mask, int32_t* evict_slots, void* stream);
 
 /* Copy the workspace's LF_DEV_* bits to *flags.  Synchronises `stream`. */
 int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags);

@@ -154,3 +154,73 @@ def test_validate_scale_and_empty_batch():
     zeros = {n: 0 for n in f.addr}
     assert f.call(shape=(0, 8, 2, 128, 100), **zeros) == lf.LF_OK
     assert f.call(shape=(2, 8, 3, 128, 100)) == lf.LF_E_SHAPE
+
+
+def _fill_call(f, nsplit=1, ws_bytes=None, scale=0.1, shape=None, **over):
+    """longflow_decode_fill on fake addresses; only argument errors are asked
+    for, which return before anything is enqueued."""
+    a = dict(f.addr, **over)
+    P = lambda x: ctypes.c_void_p(x)
+    return lf._lib.longflow_decode_fill(
+        *(shape or f.shape), scale, P(a["q"]), P(a["k"]), P(a["v"]), P(a["mask"]), P(a["nk"]), P(a["nv"]),
+        P(a["prev"]), P(a["out"]), P(a["scores"]), P(a["evict"]), P(a["ws"]),
+        f.ws_bytes if ws_bytes is None else ws_bytes, nsplit, None)
+
+
+def test_fill_argument_errors():
+    f = Fake()
+    assert _fill_call(f, nsplit=-1) == lf.LF_E_NSPLIT
+    assert _fill_call(f, nsplit=101) == lf.LF_E_NSPLIT
+    assert _fill_call(f, q=0) == lf.LF_E_NULL
+    assert _fill_call(f, out=f.addr["out"] + 2) == lf.LF_E_ALIGN
+    assert _fill_call(f, ws_bytes=f.ws_bytes - 1) == lf.LF_E_WORKSPACE
+    assert _fill_call(f, scale=float("nan")) == lf.LF_E_VALUE
+    assert _fill_call(f, shape=(2, 8, 3, 128, 100)) == lf.LF_E_SHAPE
+    zeros = {n: 0 for n in f.addr}
+    assert _fill_call(f, shape=(0, 8, 2, 128, 100), **zeros) == lf.LF_OK
+
+
+@pytest.mark.parametrize("a,b", [("mask", "q"), ("mask", "nk"), ("mask", "prev"), ("prev", "mask")])
+def test_fill_mask_is_written(a, b):
+    """The fill step writes the mask, so it may not share memory with any
+    input; the plain step only reads it."""
+    f = Fake()
+    assert _fill_call(f, **{a: f.addr[b]}) == lf.LF_E_ALIAS
+    assert f.call(**{a: f.addr[b]}) == lf.LF_OK
+
+
+def test_fill_workspace_has_free_slot_minima():
+    """Split workspaces hold one 32-bit lowest-free-slot word per combine chunk."""
+    B, Hq, Hkv, d, S = 4, 16, 2, 128, 5000
+    one = lf.lf_workspace_size(B, Hq, Hkv, d, S, 1)
+    assert one == 256
+    chunks = -(-S // 2048)
+    pairs = B * Hkv
+    gp = 8
+    split = 3
+    expect = 256
+    for n in (pairs * split * gp * 2 * 4, pairs * split * gp * d * 4, pairs * S * gp * 4, pairs * S * 4,
+              pairs * chunks * 8, pairs * chunks * 4):
+        expect += -(-n // 256) * 256
+    assert lf.lf_workspace_size(B, Hq, Hkv, d, S, split) == expect
+
+
+def _topk_call(B=2, Hkv=3, S=50, k=5, scores=1 << 40, mask=(1 << 40) + (1 << 34), out=(1 << 40) + (2 << 34)):
+    P = lambda x: ctypes.c_void_p(x)
+    return lf._lib.longflow_evict_topk(B, Hkv, S, k, P(scores), P(mask), P(out), None)
+
+
+def test_topk_argument_errors():
+    assert _topk_call(k=0) == lf.LF_E_SHAPE
+    assert _topk_call(k=51) == lf.LF_E_SHAPE
+    assert _topk_call(Hkv=0) == lf.LF_E_SHAPE
+    assert _topk_call(S=0, k=1) == lf.LF_E_SHAPE
+    assert _topk_call(B=-1) == lf.LF_E_SHAPE
+    assert _topk_call(scores=0) == lf.LF_E_NULL
+    assert _topk_call(mask=0) == lf.LF_E_NULL
+    assert _topk_call(out=0) == lf.LF_E_NULL
+    assert _topk_call(scores=(1 << 40) + 2) == lf.LF_E_ALIGN
+    assert _topk_call(out=(1 << 40) + (2 << 34) + 1) == lf.LF_E_ALIGN
+    assert _topk_call(out=(1 << 40) + 1024) == lf.LF_E_ALIAS            # inside scores
+    assert _topk_call(out=(1 << 40) + (1 << 34) + 8) == lf.LF_E_ALIAS   # inside the mask
+    assert _topk_call(B=0, scores=0, mask=0, out=0) == lf.LF_OK
