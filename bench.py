@@ -2,6 +2,7 @@
 eviction) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3_8b]
+                    [--mode decode|fill|topk|cadence]
 
 A step is one call of the operator: the KV-slot write of the previous choice,
 attention over the static cache with its mask, the per-slot scores and the
@@ -10,6 +11,14 @@ The default workload is the Qwen3-8B-shaped layer (batch 128, 32 query / 8
 KV heads, d 128, 3200 slots, bf16 K/V).  Inputs of every step are generated
 and uploaded before timing; the evicted slots go from step to step on the
 device.  Prints one JSON line.
+
+Other modes measure the cache-lifecycle entry points on the same shape:
+  fill     longflow_decode_fill on caches that start K + W slots short of
+           full and reach full at the last timed step (the mask grows by one
+           slot per sequence and step)
+  topk     longflow_evict_topk choosing --topk-k slots from synthetic scores
+  cadence  longflow_decode with the written slots taken from a top-k queue
+           refreshed every --cadence steps (periodic compression)
 """
 
 import argparse
@@ -50,16 +59,23 @@ def algorithmic_bytes(wl, mask):
             + B * Hkv * S * 4 + 2 * B * Hkv * 4)
 
 
-def measured_traffic(workload, nsplit):
+def topk_bytes(B, Hkv, S, k):
+    """Bytes one top-k launch must move: fp32 scores, the mask, the int32 list."""
+    return B * Hkv * S * 4 + B * S + k * B * Hkv * 4
+
+
+def measured_traffic(tag):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources for this workload and split."""
+    were taken on the current sources of the kernel family of this tag
+    (workload/split, or topk/workload/k)."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(f"{workload}/nsplit{nsplit}")
+            rec = json.load(f).get(tag)
     except (OSError, ValueError):
         return None
     from decode_attention_kv_05_amd.build import source_hash
-    if not rec or rec.get("kernel_hash") != source_hash():
+    family = "topk" if tag.startswith("topk/") else "decode"
+    if not rec or rec.get("kernel_hash") != source_hash(family):
         return None
     return rec.get("bytes_per_launch")
 
@@ -100,6 +116,105 @@ def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
     }
 
 
+def cpu_baseline_topk(B, Hkv, S, k, min_seconds=10.0):
+    """The oracle's k-slot selection, single-threaded, on consecutive rows of
+    the same synthetic scores until `min_seconds` of work, scaled to a launch."""
+    from decode_attention_kv_05_amd import workloads as W
+    from oracle import evict_topk
+
+    scores = W.synthetic_scores(B, Hkv, S, seed=11000, kind="ties")
+    valid = np.ones((Hkv, S), dtype=bool)
+    rows, busy, b = 0, 0.0, 0
+    while busy < min_seconds and b < B:
+        t0 = time.perf_counter()
+        evict_topk(scores[b], valid, k)
+        busy += time.perf_counter() - t0
+        rows += Hkv
+        b += 1
+    s_per_launch = busy / rows * B * Hkv
+    return {
+        "value": round(topk_bytes(B, Hkv, S, k) / s_per_launch / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{rows} of {B * Hkv} rows ({busy:.1f} s), scaled to a whole launch; numpy sort, 1 thread",
+        "s_per_launch": round(s_per_launch, 4),
+    }
+
+
+def cpu_baseline_fill(wl, max_pairs, fill_from, min_seconds=10.0):
+    """The oracle's fill step, single-threaded, on the first sequences of the
+    fill workload (same start state), consecutive steps until `min_seconds`,
+    scaled by valid K/V bytes to whole steps of the full batch."""
+    from threadpoolctl import threadpool_limits
+
+    from decode_attention_kv_05_amd import workloads as W
+    from oracle import decode_step_fill
+
+    nb = max(1, min(wl.B, -(-max_pairs // wl.Hkv)))
+    batch = list(range(nb))
+    k, v, _ = W.initial_cache(wl, batch)
+    m = (np.arange(wl.S)[None, :] < fill_from).astype(np.uint8).repeat(nb, 0)
+    W.poison_free(k, v, m)
+    prev = np.full((nb, wl.Hkv), min(fill_from, wl.S - 1), dtype=np.int32)
+    steps, busy, rows = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while busy < min_seconds and steps < wl.steps:
+            q, nk, nv = W.step_inputs(wl, steps, batch)
+            t0 = time.perf_counter()
+            _, _, prev, m = decode_step_fill(q, k, v, m, nk, nv, prev, wl.scale)
+            busy += time.perf_counter() - t0
+            rows += int(np.count_nonzero(m))
+            steps += 1
+    kv_per_row = wl.Hkv * wl.d * 2 * 2
+    rate = rows * kv_per_row / busy
+    return {
+        "value": round(rate / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{nb * wl.Hkv} of {wl.B * wl.Hkv} (sequence, KV head) pairs over {steps} fill steps "
+                  f"({busy:.1f} s), valid K/V bytes per second; numpy fp64, BLAS limited to 1 thread",
+    }
+
+
+def timed(step, K, Wm, stream, dev):
+    """Warm up, then time K steps with one event pair per step on `stream`."""
+    import torch
+    for t in range(Wm):
+        step(t)
+    torch.cuda.synchronize(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    for t in range(K):
+        starts[t].record(stream)
+        step(Wm + t)
+        ends[t].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    total_ms = starts[0].elapsed_time(ends[-1])
+    per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return total_ms / K, per_launch, wall
+
+
+def roofline(alg_bytes_per_launch, per_launch_ms, kernel, traffic):
+    launch_s = float(per_launch_ms.mean()) / 1e3
+    achieved = alg_bytes_per_launch / launch_s / 1e9
+    return {
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "kernel": kernel,
+        "launch_us_mean": round(launch_s * 1e6, 2),
+        "launch_us_p50": round(float(np.median(per_launch_ms)) * 1e3, 2),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +224,9 @@ def main():
     ap.add_argument("--nsplit", type=int, default=None, help="slot splits per pair (default: library plan)")
     ap.add_argument("--cpu-pairs", type=int, default=1024, help="oracle sample: pairs per step for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("decode", "fill", "topk", "cadence"), default="decode")
+    ap.add_argument("--topk-k", type=int, default=128, help="slots chosen per pair in topk mode")
+    ap.add_argument("--cadence", type=int, default=128, help="steps between top-k refreshes in cadence mode")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times "
                          "(calibrates HBM byte counters) and exit")
@@ -146,10 +264,18 @@ def main():
     wl = W.WORKLOADS[args.workload]
     K, Wm = args.steps, args.warmup
     log(f"device {props.name} ({props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB); "
-        f"workload {wl}")
+        f"workload {wl}; mode {args.mode}")
+    if args.mode == "topk":
+        return bench_topk(args, wl, lf, W, dev)
 
     t0 = time.time()
     k, v, mask = W.initial_cache(wl)
+    fill_from = None
+    if args.mode == "fill":
+        # every sequence starts K + W slots short of full and fills up by the last step
+        fill_from = max(1, wl.S - (K + Wm))
+        mask = (np.arange(wl.S)[None, :] < fill_from).astype(np.uint8).repeat(wl.B, 0)
+        W.poison_free(k, v, mask)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     dk, dv = to_dev(k), to_dev(v)
     del k, v
@@ -170,41 +296,59 @@ def main():
     slots = [torch.full((wl.B, wl.Hkv), -1, dtype=torch.int32, device=dev),
              torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev)]
     stream = torch.cuda.current_stream(dev)
+    N = args.cadence
+    queue = torch.full((N, wl.B, wl.Hkv), -1, dtype=torch.int32, device=dev)
+
+    if args.mode == "fill":
+        slots[0].fill_(fill_from if fill_from < wl.S else -1)
 
     def step(t):
         i = t % n_inputs
-        lf.longflow_decode(qs[i], dk, dv, dm, nks[i], nvs[i], slots[t % 2], scale=float(wl.scale),
-                           out=out, scores=scores, evict_slot=slots[(t + 1) % 2], workspace=ws,
-                           nsplit=nsplit, stream=stream)
+        if args.mode == "decode":
+            lf.longflow_decode(qs[i], dk, dv, dm, nks[i], nvs[i], slots[t % 2], scale=float(wl.scale),
+                               out=out, scores=scores, evict_slot=slots[(t + 1) % 2], workspace=ws,
+                               nsplit=nsplit, stream=stream)
+        elif args.mode == "fill":
+            lf.longflow_decode_fill(qs[i], dk, dv, dm, nks[i], nvs[i], slots[t % 2], scale=float(wl.scale),
+                                    out=out, scores=scores, next_slot=slots[(t + 1) % 2], workspace=ws,
+                                    nsplit=nsplit, stream=stream)
+        else:  # cadence: the written slot comes from the queue of the last refresh
+            lf.longflow_decode(qs[i], dk, dv, dm, nks[i], nvs[i], queue[t % N], scale=float(wl.scale),
+                               out=out, scores=scores, evict_slot=slots[0], workspace=ws,
+                               nsplit=nsplit, stream=stream)
+            if (t + 1) % N == 0:
+                lf.longflow_evict_topk(scores, dm, N, out=queue, stream=stream)
 
-    for t in range(Wm):
-        step(t)
-    torch.cuda.synchronize(dev)
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize(dev)
-    wall0 = time.perf_counter()
-    for t in range(K):
-        starts[t].record(stream)
-        step(Wm + t)
-        ends[t].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - wall0
-    total_ms = starts[0].elapsed_time(ends[-1])
-    per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    ms_per_step = total_ms / K
+    ms_per_step, per_launch, wall = timed(step, K, Wm, stream, dev)
     status = lf.lf_read_device_status(ws)
     if status:
         raise RuntimeError(f"device status flags set during the run: {status:#x}")
 
-    kvb = kv_bytes(wl, mask)
-    algb = algorithmic_bytes(wl, mask)
-    launch_s = float(per_launch.mean()) / 1e3
-    achieved = algb / launch_s / 1e9
-    traffic = measured_traffic(wl.name, nsplit)
+    if args.mode == "fill":
+        # valid rows of step t (warm-up included): the prefix plus the t + 1 written slots
+        rows = sum(min(wl.S, fill_from + t + 1) for t in range(Wm, Wm + K)) / K
+        kvb = int(rows * wl.B * wl.Hkv * wl.d * 2 * 2)
+        final_mask = dm.cpu().numpy()
+        if not final_mask.all() and fill_from + Wm + K >= wl.S:
+            raise RuntimeError("fill run ended with free slots left")
+        algb = kvb + algorithmic_bytes(wl, np.zeros_like(mask)) + wl.B
+    else:
+        kvb = kv_bytes(wl, mask)
+        algb = algorithmic_bytes(wl, mask)
+    if args.mode == "cadence":
+        # decode launches only: top-k launches are timed inside the steps that run them
+        dec = np.array([x for t, x in enumerate(per_launch) if (Wm + t + 1) % N != 0])
+        rl = roofline(algb, dec if dec.size else per_launch, "longflow_decode_kernel", None)
+    else:
+        rl = roofline(algb, per_launch, "longflow_decode_kernel",
+                      measured_traffic(f"{wl.name}/nsplit{nsplit}" + ("/fill" if args.mode == "fill" else "")))
+    metric = {
+        "decode": METRIC,
+        "fill": "fill-phase decode-attn+next slot: KV GB/s, steps/s at B=128, 3200 slots",
+        "cadence": f"decode-attn with top-k eviction every {N} steps: KV GB/s, steps/s at B=128, 3200 slots",
+    }[args.mode]
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(kvb / (ms_per_step / 1e3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -226,23 +370,63 @@ def main():
         "alg_GBps": round(algb / (ms_per_step / 1e3) / 1e9, 2),
         "pct_hbm_peak": round(100 * algb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
         "alg_bytes_per_step": algb,
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel": "longflow_decode_kernel",
-            "launch_us_mean": round(launch_s * 1e6, 2),
-            "launch_us_p50": round(float(np.median(per_launch)) * 1e3, 2),
-        },
+        "roofline": rl,
+        "wall_s_timed": round(wall, 3),
+    }
+    if args.mode == "fill":
+        result["config"].update({"mode": "fill", "start_valid_slots": fill_from})
+    if args.mode == "cadence":
+        result["config"].update({"mode": "cadence", "cadence": N})
+        refresh = [x for t, x in enumerate(per_launch) if (Wm + t + 1) % N == 0]
+        if refresh:
+            result["refresh_step_us_mean"] = round(float(np.mean(refresh)) * 1e3, 2)
+    if not args.no_cpu_baseline and args.mode != "cadence":
+        t0 = time.time()
+        if args.mode == "fill":
+            result["cpu_baseline"] = cpu_baseline_fill(wl, args.cpu_pairs, fill_from)
+        else:
+            result["cpu_baseline"] = cpu_baseline(wl, mask, args.cpu_pairs)
+        log(f"cpu baseline took {time.time() - t0:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
+def bench_topk(args, wl, lf, W, dev):
+    """k-slot selection over synthetic scores of the workload's shape."""
+    import torch
+    B, Hkv, S, k = wl.B, wl.Hkv, wl.S, args.topk_k
+    K, Wm = args.steps, args.warmup
+    scores = torch.from_numpy(W.synthetic_scores(B, Hkv, S, seed=11000, kind="ties")).to(dev)
+    mask = torch.ones((B, S), dtype=torch.uint8, device=dev)
+    out = torch.empty((k, B, Hkv), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        lf.longflow_evict_topk(scores, mask, k, out=out, stream=stream)
+
+    ms, per_launch, wall = timed(step, K, Wm, stream, dev)
+    algb = topk_bytes(B, Hkv, S, k)
+    result = {
+        "metric": f"k-slot eviction (k={k}): scores GB/s, launches/s at B={B}, {S} slots",
+        "value": round(algb / (ms / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "mode": "topk", "batch": B, "kv_heads": Hkv, "slots": S, "k": k,
+                   "scores": "ties"},
+        "steps_per_s": round(1e3 / ms, 2),
+        "alg_bytes_per_step": algb,
+        "roofline": roofline(algb, per_launch, "evict_topk_kernel", measured_traffic(f"topk/{wl.name}/k{k}")),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        t0 = time.time()
-        result["cpu_baseline"] = cpu_baseline(wl, mask, args.cpu_pairs)
-        log(f"cpu baseline took {time.time() - t0:.1f} s")
+        result["cpu_baseline"] = cpu_baseline_topk(B, Hkv, S, k)
     print(json.dumps(result), flush=True)
 
 

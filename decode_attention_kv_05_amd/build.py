@@ -21,12 +21,22 @@ SOURCES = [os.path.join(CSRC, "longflow_api.cpp"), os.path.join(CSRC, "longflow_
 ARCH = "gfx950"
 
 
-def source_hash():
-    """Short hash of the kernel and host sources (identifies a kernel build)."""
+# Sources each kernel family's code depends on (the host API and the shared
+# headers count for every family).
+_COMMON = ["longflow_api.cpp", "layout.h", "launch.h"]
+_FAMILIES = {"decode": ["longflow_kernels.hip"], "topk": ["evict_topk.hip"]}
+
+
+def source_hash(family=None):
+    """Short hash of the sources of one kernel family ("decode", "topk"), or
+    of the whole library when family is None; identifies a kernel build."""
     import hashlib
+    if family is None:
+        names = _COMMON + [n for v in _FAMILIES.values() for n in v]
+    else:
+        names = _COMMON + _FAMILIES[family]
     h = hashlib.sha256()
-    for path in sorted(SOURCES + [os.path.join(CSRC, n) for n in ("layout.h", "launch.h")]
-                       + [os.path.join(INCLUDE, "longflow.h")]):
+    for path in sorted([os.path.join(CSRC, n) for n in names] + [os.path.join(INCLUDE, "longflow.h")]):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -1,17 +1,21 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
     python -m decode_attention_kv_05_amd.profile_summary stats DIR --workload W --command "..."
+        [--name STEM]
     python -m decode_attention_kv_05_amd.profile_summary traffic --workload W --nsplit N \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes BYTES --command "..."
+        [--name STEM] [--kernel SUBSTRING] [--tag KEY]
 
 `stats` reads a `rocprofv3 --kernel-trace --stats --output-format csv` run and
-writes profiles/longflow_decode_<W>_kernels.txt.  `traffic` reads four
-`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (the decode benchmark
-and a plain device copy of a known size, run with `bench.py --copy-probe`),
-scales the decode kernel's per-dispatch KiB by bytes-copied / KiB-counted of
-the copy, and writes profiles/longflow_decode_<W>_traffic.txt plus an entry of
-profiles/traffic.json tagged with the hash of the kernel sources it measured
-(bench.py reports the figure only while that hash matches).
+writes profiles/<STEM>_kernels.txt (STEM defaults to longflow_decode_<W>).
+`traffic` reads four `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs
+(the benchmark and a plain device copy of a known size, run with `bench.py
+--copy-probe`), scales the per-dispatch KiB of the kernel whose name contains
+SUBSTRING (default: the decode kernel) by bytes-copied / KiB-counted of the
+copy, and writes profiles/<STEM>_traffic.txt plus the entry KEY (default
+<W>/nsplit<N>) of profiles/traffic.json, tagged with the hash of the kernel
+sources it measured (bench.py reports the figure only while that hash
+matches).
 """
 
 import argparse
@@ -68,17 +72,22 @@ def dispatch_durations(directory):
     return out
 
 
+def _family(args):
+    text = f"{args.name or ''} {getattr(args, 'kernel', None) or ''}"
+    return "topk" if "topk" in text else "decode"
+
+
 def write_stats(args):
     rows = _rows(_find(args.dir, "kernel_stats.csv"))
     try:
         trace = dispatch_durations(args.dir)
     except FileNotFoundError:
         trace = {}
-    out = os.path.join(PROFILES, f"longflow_decode_{args.workload}_kernels.txt")
+    out = os.path.join(PROFILES, f"{args.name or 'longflow_decode_' + args.workload}_kernels.txt")
     with open(out, "w") as f:
         f.write(f"# rocprofv3 kernel statistics, workload {args.workload}\n")
         f.write(f"# command: {args.command}\n")
-        f.write(f"# kernel sources: {source_hash()}  date: {time.strftime('%Y-%m-%d')}\n")
+        f.write(f"# kernel sources ({_family(args)}): {source_hash(_family(args))}  date: {time.strftime('%Y-%m-%d')}\n")
         f.write("# avg/min/max over every dispatch (warm-up included); p50 = median dispatch from the kernel trace\n")
         f.write(f"{'calls':>6} {'avg_us':>10} {'p50_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel\n")
         for r in rows:
@@ -95,8 +104,9 @@ def write_traffic(args):
     write = counter_means(args.write, "WRITE_SIZE")
     cfetch = counter_means(args.copy_fetch, "FETCH_SIZE")
     cwrite = counter_means(args.copy_write, "WRITE_SIZE")
-    is_decode = lambda n: DECODE in n
-    is_copy = lambda n: any(h in n.lower() for h in COPY_HINTS) and DECODE not in n
+    want = args.kernel or DECODE
+    is_decode = lambda n: want in n
+    is_copy = lambda n: any(h in n.lower() for h in COPY_HINTS) and want not in n
     kname, (f_kib, nf) = _pick(fetch, is_decode)
     _, (w_kib, nw) = _pick(write, is_decode)
     cname, (cf_kib, _) = _pick(cfetch, is_copy)
@@ -106,14 +116,15 @@ def write_traffic(args):
     read_b = f_kib * 1024.0 * f_scale
     write_b = w_kib * 1024.0 * w_scale
     total = read_b + write_b
-    tag = f"{args.workload}/nsplit{args.nsplit}"
-    out = os.path.join(PROFILES, f"longflow_decode_{args.workload}_traffic.txt")
+    tag = args.tag or f"{args.workload}/nsplit{args.nsplit}"
+    out = os.path.join(PROFILES, f"{args.name or 'longflow_decode_' + args.workload}_traffic.txt")
     with open(out, "w") as f:
-        f.write(f"# HBM traffic of {kname[:80]} from rocprofv3 counters, workload {args.workload}, nsplit {args.nsplit}\n")
+        f.write(f"# HBM traffic of {kname[:80]} from rocprofv3 counters, workload {args.workload}, "
+                f"nsplit {args.nsplit}, key {tag}\n")
         f.write(f"# commands: {args.command}\n")
-        f.write(f"# kernel sources: {source_hash()}  date: {time.strftime('%Y-%m-%d')}\n")
-        f.write(f"FETCH_SIZE KiB/dispatch (decode, mean of {nf}): {f_kib:.1f}\n")
-        f.write(f"WRITE_SIZE KiB/dispatch (decode, mean of {nw}): {w_kib:.1f}\n")
+        f.write(f"# kernel sources ({_family(args)}): {source_hash(_family(args))}  date: {time.strftime('%Y-%m-%d')}\n")
+        f.write(f"FETCH_SIZE KiB/dispatch (mean of {nf}): {f_kib:.1f}\n")
+        f.write(f"WRITE_SIZE KiB/dispatch (mean of {nw}): {w_kib:.1f}\n")
         f.write(f"copy probe {cname[:60]}: {args.copy_bytes} bytes; FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB\n")
         f.write(f"scale factors (bytes per counted byte): fetch {f_scale:.4f}, write {w_scale:.4f}\n")
         f.write(f"HBM bytes per launch: read {read_b:.0f}, write {write_b:.0f}, total {total:.0f}\n")
@@ -123,7 +134,7 @@ def write_traffic(args):
             db = json.load(f)
     except (OSError, ValueError):
         db = {}
-    db[tag] = {"kernel_hash": source_hash(), "bytes_per_launch": round(total), "read_bytes": round(read_b),
+    db[tag] = {"kernel_hash": source_hash(_family(args)), "bytes_per_launch": round(total), "read_bytes": round(read_b),
                "write_bytes": round(write_b), "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5)}
     with open(path, "w") as f:
         json.dump(db, f, indent=1, sort_keys=True)
@@ -138,11 +149,15 @@ def main():
     s.add_argument("dir")
     s.add_argument("--workload", required=True)
     s.add_argument("--command", required=True)
+    s.add_argument("--name", default=None)
     t = sub.add_parser("traffic")
     for k in ("workload", "fetch", "write", "copy_fetch", "copy_write", "command"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--nsplit", type=int, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--name", default=None)
+    t.add_argument("--kernel", default=None)
+    t.add_argument("--tag", default=None)
     args = ap.parse_args()
     (write_stats if args.cmd == "stats" else write_traffic)(args)
 
