@@ -5,6 +5,8 @@
     python -m decode_attention_kv_05_amd.profile_summary traffic --workload W --nsplit N \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes BYTES --command "..."
         [--name STEM] [--kernel SUBSTRING] [--tag KEY]
+    python -m decode_attention_kv_05_amd.profile_summary counters DIR [DIR ...] --kernel SUBSTRING \
+        --name STEM --command "..."
 
 `stats` reads a `rocprofv3 --kernel-trace --stats --output-format csv` run and
 writes profiles/<STEM>_kernels.txt (STEM defaults to longflow_decode_<W>).
@@ -142,6 +144,44 @@ def write_traffic(args):
     print(out)
 
 
+def write_counters(args):
+    """Mean per-dispatch value of every counter found in the given --pmc runs,
+    for the kernel whose name contains --kernel, plus a few ratios."""
+    vals = {}
+    kname = None
+    for d in args.dirs:
+        for row in _rows(_find(d, "counter_collection.csv")):
+            if args.kernel not in row["Kernel_Name"]:
+                continue
+            kname = row["Kernel_Name"]
+            vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    if not vals:
+        raise KeyError(f"no counters for a kernel matching {args.kernel!r}")
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    out = os.path.join(PROFILES, f"{args.name}_counters.txt")
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 hardware counters of {kname[:90]}\n")
+        f.write(f"# command: {args.command}\n")
+        f.write(f"# kernel sources ({_family(args)}): {source_hash(_family(args))}  date: {time.strftime('%Y-%m-%d')}\n")
+        f.write("# mean per dispatch over all dispatches of the kernel (summed over the device)\n")
+        for k in sorted(mean):
+            f.write(f"{k:28s} {mean[k]:18.1f}   ({len(vals[k])} dispatches)\n")
+        ratios = [
+            ("LDS bank-conflict cycles / LDS active cycles", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+            ("LDS address-conflict cycles / LDS active cycles", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+            ("LDS instructions per VALU instruction", "SQ_INSTS_LDS", "SQ_INSTS_VALU"),
+            ("VALU instructions per wave", "SQ_INSTS_VALU", "SQ_WAVES"),
+            ("vector-memory read instructions per wave", "SQ_INSTS_VMEM_RD", "SQ_WAVES"),
+            ("VALU-active cycles / wave cycles", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+            ("LDS-wait cycles / wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+        ]
+        f.write("# ratios\n")
+        for label, a, b in ratios:
+            if a in mean and b in mean and mean[b]:
+                f.write(f"{label:52s} {mean[a] / mean[b]:10.4f}\n")
+    print(out)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -158,8 +198,13 @@ def main():
     t.add_argument("--name", default=None)
     t.add_argument("--kernel", default=None)
     t.add_argument("--tag", default=None)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--name", required=True)
+    c.add_argument("--command", required=True)
     args = ap.parse_args()
-    (write_stats if args.cmd == "stats" else write_traffic)(args)
+    {"stats": write_stats, "traffic": write_traffic, "counters": write_counters}[args.cmd](args)
 
 
 if __name__ == "__main__":
