@@ -19,6 +19,11 @@ Other modes measure the cache-lifecycle entry points on the same shape:
   topk     longflow_evict_topk choosing --topk-k slots from synthetic scores
   cadence  longflow_decode with the written slots taken from a top-k queue
            refreshed every --cadence steps (periodic compression)
+  stack    the attention module of a Qwen3-8B-shaped model: --layers layers
+           (default 36) of QKV projection, RoPE, the LongFlow step and the
+           output projection with residual, replayed as one HIP graph per
+           token (synthetic weights; every layer's cache starts as a copy of
+           the workload's cache)
 """
 
 import argparse
@@ -224,7 +229,9 @@ def main():
     ap.add_argument("--nsplit", type=int, default=None, help="slot splits per pair (default: library plan)")
     ap.add_argument("--cpu-pairs", type=int, default=1024, help="oracle sample: pairs per step for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("decode", "fill", "topk", "cadence"), default="decode")
+    ap.add_argument("--mode", choices=("decode", "fill", "topk", "cadence", "stack"), default="decode")
+    ap.add_argument("--layers", type=int, default=36, help="layers in stack mode")
+    ap.add_argument("--hidden", type=int, default=4096, help="model width in stack mode")
     ap.add_argument("--topk-k", type=int, default=128, help="slots chosen per pair in topk mode")
     ap.add_argument("--cadence", type=int, default=128, help="steps between top-k refreshes in cadence mode")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -267,6 +274,8 @@ def main():
         f"workload {wl}; mode {args.mode}")
     if args.mode == "topk":
         return bench_topk(args, wl, lf, W, dev)
+    if args.mode == "stack":
+        return bench_stack(args, wl, lf, W, dev)
 
     t0 = time.time()
     k, v, mask = W.initial_cache(wl)
@@ -427,6 +436,117 @@ def bench_topk(args, wl, lf, W, dev):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_topk(B, Hkv, S, k)
+    print(json.dumps(result), flush=True)
+
+
+
+def stack_weight_bytes(L, H, Hq, Hkv, d):
+    return L * ((Hq + 2 * Hkv) * d * H + H * Hq * d) * 2
+
+
+def cpu_baseline_stack(wl, L, H, min_seconds=10.0):
+    """The oracle's multi-layer step, single-threaded, on one sequence at a
+    time (sequences are independent) until `min_seconds`, scaled to the batch."""
+    from threadpoolctl import threadpool_limits
+
+    from decode_attention_kv_05_amd import workloads as W
+    from oracle.stack_oracle import stack_step
+
+    weights = [W.layer_weights(wl.seed, l, H, wl.Hq, wl.Hkv, wl.d) for l in range(L)]
+    done, busy = 0, 0.0
+    with threadpool_limits(limits=1):
+        while busy < min_seconds and done < wl.B:
+            k, v, m = W.initial_cache(wl, [done])
+            layers = [{"w_qkv": wq, "w_o": wo, "k": k.copy(), "v": v.copy(), "mask": m,
+                       "slot": np.full((1, wl.Hkv), -1, np.int32)} for wq, wo in weights]
+            x = W.token_activations(wl.seed, 0, wl.B, H)[done:done + 1]
+            t0 = time.perf_counter()
+            stack_step(x, np.array([wl.S]), layers, wl.Hq, wl.Hkv, wl.d, wl.scale, 1e6)
+            busy += time.perf_counter() - t0
+            done += 1
+    s_per_step = busy / done * wl.B
+    kvb = kv_bytes(wl, np.ones((wl.B, wl.S), np.uint8)) * L
+    return {
+        "value": round(kvb / s_per_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {wl.B} sequences through all {L} layers ({busy:.1f} s), scaled to the batch; "
+                  f"numpy fp64, BLAS limited to 1 thread",
+        "s_per_step": round(s_per_step, 2),
+    }
+
+
+def bench_stack(args, wl, lf, W, dev):
+    """--layers layers of the attention module around the operator, replayed
+    as one HIP graph per token."""
+    import torch
+    L, H = args.layers, args.hidden
+    K, Wm = args.steps, args.warmup
+    t0 = time.time()
+    k, v, mask = W.initial_cache(wl)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    dk0, dv0 = to_dev(k), to_dev(v)
+    del k, v
+    dm = torch.from_numpy(mask).to(dev)
+    kc = [dk0] + [dk0.clone() for _ in range(L - 1)]
+    vc = [dv0] + [dv0.clone() for _ in range(L - 1)]
+    wq, wo = [], []
+    for l in range(L):
+        a, b = W.layer_weights(wl.seed, l, H, wl.Hq, wl.Hkv, wl.d)
+        wq.append(to_dev(a))
+        wo.append(to_dev(b))
+    n_inputs = max(1, min(16, K + Wm))
+    xs = [to_dev(W.token_activations(wl.seed, t, wl.B, H)) for t in range(n_inputs)]
+    x_in = torch.empty((wl.B, H), dtype=torch.bfloat16, device=dev)
+    x_out = torch.empty_like(x_in)
+    pos = torch.full((wl.B,), wl.S, dtype=torch.int32, device=dev)
+    slots = [torch.full((wl.B, wl.Hkv), -1, dtype=torch.int32, device=dev) for _ in range(L)]
+    nsplit = args.nsplit or lf.plan_nsplit(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S)
+    stack = lf.Stack(x_in, x_out, pos, wq, wo, kc, vc, [dm] * L, slots, None, Hq=wl.Hq,
+                     scale=float(wl.scale), rope_base=1e6, nsplit=nsplit)
+    graph = stack.graph()
+    log(f"{L} layers set up in {time.time() - t0:.1f} s")
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        x_in.copy_(xs[t % n_inputs], non_blocking=True)
+        graph.launch(stream)
+
+    ms, per_launch, wall = timed(step, K, Wm, stream, dev)
+    status = lf.lf_read_device_status(stack.tensors["workspace"])
+    graph.close()
+    if status:
+        raise RuntimeError(f"device status flags set during the run: {status:#x}")
+    kvb = kv_bytes(wl, mask) * L
+    wb = stack_weight_bytes(L, H, wl.Hq, wl.Hkv, wl.d)
+    algb = algorithmic_bytes(wl, mask) * L + wb + 2 * wl.B * H * 2
+    result = {
+        "metric": f"{L}-layer attention module (QKV proj + RoPE + LongFlow step + O proj): KV GB/s, "
+                  f"tokens/s at B={wl.B}, {wl.S} slots",
+        "value": round(kvb / (ms / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "mode": "stack", "layers": L, "hidden": H, "batch": wl.B,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d, "slots": wl.S, "nsplit": nsplit,
+                   "weights": "synthetic N(0, 1/fan_in)", "launch": "one HIP graph per token"},
+        "tokens_per_s": round(wl.B * 1e3 / ms, 1),
+        "steps_per_s": round(1e3 / ms, 2),
+        "alg_bytes_per_step": algb,
+        "weight_bytes_per_step": wb,
+        "roofline": roofline(algb, per_launch, f"{L}-layer step (graph)", None),
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_stack(wl, L, H)
     print(json.dumps(result), flush=True)
 
 

@@ -16,27 +16,32 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblongflow.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "longflow_api.cpp"), os.path.join(CSRC, "longflow_kernels.hip"),
-           os.path.join(CSRC, "evict_topk.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("longflow_api.cpp", "longflow_kernels.hip", "evict_topk.hip",
+                                            "stack_api.cpp", "stack_kernels.hip")]
 ARCH = "gfx950"
 
 
 # Sources each kernel family's code depends on (the host API and the shared
 # headers count for every family).
 _COMMON = ["longflow_api.cpp", "layout.h", "launch.h"]
-_FAMILIES = {"decode": ["longflow_kernels.hip"], "topk": ["evict_topk.hip"]}
+_FAMILIES = {"decode": ["longflow_kernels.hip"], "topk": ["evict_topk.hip"],
+             "stack": ["longflow_kernels.hip", "stack_api.cpp", "stack_kernels.hip"]}
+_HEADERS = {"decode": ["longflow.h"], "topk": ["longflow.h"], "stack": ["longflow.h", "longflow_stack.h"]}
 
 
 def source_hash(family=None):
-    """Short hash of the sources of one kernel family ("decode", "topk"), or
-    of the whole library when family is None; identifies a kernel build."""
+    """Short hash of the sources of one kernel family ("decode", "topk",
+    "stack"), or of the whole library when family is None; identifies a
+    kernel build."""
     import hashlib
     if family is None:
-        names = _COMMON + [n for v in _FAMILIES.values() for n in v]
+        names = _COMMON + sorted({n for v in _FAMILIES.values() for n in v})
+        headers = sorted({n for v in _HEADERS.values() for n in v})
     else:
         names = _COMMON + _FAMILIES[family]
+        headers = _HEADERS[family]
     h = hashlib.sha256()
-    for path in sorted([os.path.join(CSRC, n) for n in names] + [os.path.join(INCLUDE, "longflow.h")]):
+    for path in sorted([os.path.join(CSRC, n) for n in names] + [os.path.join(INCLUDE, n) for n in headers]):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

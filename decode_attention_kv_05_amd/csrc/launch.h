@@ -38,8 +38,48 @@ struct TopkParams {
   int Hkv, S, k, pairs;
 };
 
+// C[M][N] = A[M][K] W[N][K]^T (+ R[M][N] when r is set), all bf16; part is
+// an fp32 workspace of gemm_partial_bytes(M, N, K) bytes.  N % 16 == 0,
+// K % 256 == 0, M <= 256.
+struct GemmParams {
+  const uint16_t* a;
+  const uint16_t* w;
+  const uint16_t* r;
+  uint16_t* c;
+  float* part;
+  int M, N, K;
+  int ksplit, kslice;  // set by launch_gemm
+};
+int gemm_ksplit(int N, int K);
+size_t gemm_partial_bytes(int M, int N, int K);
+
+// qkv [B][(Hq + 2 Hkv) d] -> q [B][Hq][d], k, v [B][Hkv][d]; q and k rotated.
+struct RopeParams {
+  const uint16_t* qkv;
+  const int32_t* pos;
+  uint16_t* q;
+  uint16_t* k;
+  uint16_t* v;
+  int B, Hq, Hkv, d;
+  double log2_base;
+};
+
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
                          hipStream_t stream);
+hipError_t launch_gemm(const GemmParams& prm, hipStream_t stream);
+hipError_t launch_rope_split(const RopeParams& prm, hipStream_t stream);
+hipError_t launch_advance_pos(int32_t* pos, int n, hipStream_t stream);
+
+// One decode step after validation (the decode kernel and, for several
+// splits, the combine and finalize kernels).  mask_w non-null selects the
+// fill step.  evict_slot may equal prev_slot outside the fill step: every
+// split reads its pair's prev_slot before the pair's evicted slot is
+// written (by the same workgroup at its end, or by the finalize kernel).
+int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                        void* k_cache, void* v_cache, const uint8_t* mask, uint8_t* mask_w,
+                        const void* new_k, const void* new_v, const int32_t* prev_slot, void* out,
+                        float* scores, int32_t* evict_slot, void* workspace, int nsplit,
+                        void* stream);
 hipError_t launch_topk(const TopkParams& prm, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 

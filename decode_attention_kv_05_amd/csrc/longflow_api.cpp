@@ -188,9 +188,13 @@ int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void*
   return LF_OK;
 }
 
+}  // namespace
+
+namespace lf {
+
 // Enqueue one step after validation: the decode kernel, and for several
 // splits the combine and finalize kernels.
-int enqueue_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q, void* k_cache,
+int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q, void* k_cache,
                  void* v_cache, const uint8_t* mask, uint8_t* mask_w, const void* new_k,
                  const void* new_v, const int32_t* prev_slot, void* out, float* scores,
                  int32_t* evict_slot, void* workspace, int nsplit, void* stream) {
@@ -239,7 +243,7 @@ int enqueue_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* 
              : LF_E_HIP;
 }
 
-}  // namespace
+}  // namespace lf
 
 extern "C" {
 
@@ -261,7 +265,7 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
                        prev_slot, out, scores, evict_slot, workspace, workspace_bytes, nsplit);
   if (rc != LF_OK) return rc;
   if (B == 0) return LF_OK;
-  return enqueue_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, nullptr, new_k, new_v,
+  return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, nullptr, new_k, new_v,
                       prev_slot, out, scores, evict_slot, workspace, nsplit, stream);
 }
 
@@ -302,7 +306,7 @@ int longflow_decode_fill(int B, int Hq, int Hkv, int d, int S, float scale, cons
   rc = validate_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v, prev_slot,
                      out, scores, next_slot, workspace, workspace_bytes, nsplit, true);
   if (rc != LF_OK) return rc;
-  return enqueue_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, mask, new_k, new_v,
+  return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, mask, new_k, new_v,
                       prev_slot, out, scores, next_slot, workspace, nsplit, stream);
 }
 

@@ -31,6 +31,8 @@ EXPORTED = (
     "lf_version", "lf_strerror", "lf_check_shape", "lf_plan_nsplit", "lf_workspace_size",
     "lf_device_num_cus", "lf_workspace_init", "lf_validate", "longflow_decode",
     "longflow_decode_nsplit", "longflow_decode_fill", "longflow_evict_topk", "lf_read_device_status",
+    "lf_stack_workspace_size", "longflow_stack_step", "lf_stack_graph_create", "lf_graph_launch",
+    "lf_graph_destroy",
 )
 
 _i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -54,6 +56,12 @@ def _load():
         "longflow_decode_fill": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i, _p], _i),
         "longflow_evict_topk": ([_i] * 4 + [_p] * 3 + [_p], _i),
         "lf_read_device_status": ([_p, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
+        "lf_stack_workspace_size": ([_i] * 8 + [ctypes.POINTER(_sz)], _i),
+        "longflow_stack_step": ([_i] * 7 + [_f, _f] + [_p] * 3 + [_i] + [_p] * 8 + [_sz, _i, _p], _i),
+        "lf_stack_graph_create": ([_i] * 7 + [_f, _f] + [_p] * 3 + [_i] + [_p] * 8 + [_sz, _i,
+                                                                             ctypes.POINTER(_p)], _i),
+        "lf_graph_launch": ([_p, _p], _i),
+        "lf_graph_destroy": ([_p], _i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -245,3 +253,102 @@ def lf_read_device_status(workspace, stream=None):
     _check(_lib.lf_read_device_status(ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream, workspace.device),
                                       ctypes.byref(flags)), "lf_read_device_status")
     return flags.value
+
+
+def lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, nsplit):
+    out = _sz(0)
+    _check(_lib.lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, nsplit, ctypes.byref(out)),
+           "lf_stack_workspace_size")
+    return out.value
+
+
+class Stack:
+    """Argument marshalling for the multi-layer step (include/longflow_stack.h).
+
+    Holds the per-layer device tensors and the host pointer arrays built from
+    them; `step()` enqueues one eager step, `graph()` records one into a HIP
+    graph (a StackGraph).  Tensors: x_in, x_out [B, H] bf16; pos [B] int32;
+    per layer w_qkv [(Hq + 2 Hkv) d, H], w_o [H, Hq d] bf16, k_cache,
+    v_cache [B, Hkv, S, d] bf16, mask [B, S] uint8, slot [B, Hkv] int32,
+    scores [B, Hkv, S] float32 or None.
+    """
+
+    def __init__(self, x_in, x_out, pos, w_qkv, w_o, k_cache, v_cache, mask, slot, scores=None, *,
+                 Hq, scale=None, rope_base=1e6, advance_pos=True, nsplit=None, workspace=None):
+        L = len(w_qkv)
+        B, H = x_in.shape
+        Hkv, S, d = k_cache[0].shape[1], k_cache[0].shape[2], k_cache[0].shape[3]
+        dev = x_in.device
+        _need(x_in, "x_in", torch.bfloat16, (B, H), dev)
+        _need(x_out, "x_out", torch.bfloat16, (B, H), dev)
+        _need(pos, "pos", torch.int32, (B,), dev)
+        for name, lst in (("w_qkv", w_qkv), ("w_o", w_o), ("k_cache", k_cache), ("v_cache", v_cache),
+                          ("mask", mask), ("slot", slot)):
+            if len(lst) != L:
+                raise ValueError(f"{name} has {len(lst)} entries, expected {L}")
+        for l in range(L):
+            _need(w_qkv[l], "w_qkv", torch.bfloat16, ((Hq + 2 * Hkv) * d, H), dev)
+            _need(w_o[l], "w_o", torch.bfloat16, (H, Hq * d), dev)
+            _need(k_cache[l], "k_cache", torch.bfloat16, (B, Hkv, S, d), dev)
+            _need(v_cache[l], "v_cache", torch.bfloat16, (B, Hkv, S, d), dev)
+            _need(mask[l], "mask", (torch.uint8, torch.bool), (B, S), dev)
+            _need(slot[l], "slot", torch.int32, (B, Hkv), dev)
+            if scores is not None and scores[l] is not None:
+                _need(scores[l], "scores", torch.float32, (B, Hkv, S), dev)
+        if nsplit is None:
+            nsplit = plan_nsplit(B, Hq, Hkv, d, S)
+        if workspace is None:
+            workspace = torch.zeros(lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, nsplit), dtype=torch.uint8,
+                                    device=dev)
+        self.dims = (L, B, H, Hq, Hkv, d, S)
+        self.scale = float(scale if scale is not None else 1.0 / float(d) ** 0.5)
+        self.rope_base = float(rope_base)
+        self.advance_pos = 1 if advance_pos else 0
+        self.nsplit = int(nsplit)
+        self.tensors = dict(x_in=x_in, x_out=x_out, pos=pos, w_qkv=list(w_qkv), w_o=list(w_o),
+                            k_cache=list(k_cache), v_cache=list(v_cache), mask=list(mask), slot=list(slot),
+                            scores=list(scores) if scores is not None else None, workspace=workspace)
+        arr = lambda ts: (_p * L)(*[t.data_ptr() if t is not None else None for t in ts])
+        self._arrays = [arr(w_qkv), arr(w_o), arr(k_cache), arr(v_cache), arr(mask), arr(slot),
+                        arr(scores) if scores is not None else None]
+
+    def _args(self):
+        t = self.tensors
+        P = lambda x: ctypes.c_void_p(x.data_ptr())
+        a = self._arrays
+        return (*self.dims, self.scale, self.rope_base, P(t["x_in"]), P(t["x_out"]), P(t["pos"]),
+                self.advance_pos, a[0], a[1], a[2], a[3], a[4], a[5], a[6], P(t["workspace"]),
+                t["workspace"].numel(), self.nsplit)
+
+    def step(self, stream=None):
+        _check(_lib.longflow_stack_step(*self._args(), _stream_ptr(stream, self.tensors["x_in"].device)),
+               "longflow_stack_step")
+
+    def graph(self):
+        return StackGraph(self)
+
+
+class StackGraph:
+    """A recorded step (lf_stack_graph_create); launch() replays it."""
+
+    def __init__(self, stack):
+        self.stack = stack  # keeps every tensor the graph points at alive
+        h = _p(0)
+        _check(_lib.lf_stack_graph_create(*stack._args(), ctypes.byref(h)), "lf_stack_graph_create")
+        self.handle = h
+
+    def launch(self, stream=None):
+        _check(_lib.lf_graph_launch(self.handle, _stream_ptr(stream, self.stack.tensors["x_in"].device)),
+               "lf_graph_launch")
+
+    def close(self):
+        if self.handle:
+            torch.cuda.synchronize()
+            _check(_lib.lf_graph_destroy(self.handle), "lf_graph_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -76,7 +76,10 @@ def dispatch_durations(directory):
 
 def _family(args):
     text = f"{args.name or ''} {getattr(args, 'kernel', None) or ''}"
-    return "topk" if "topk" in text else "decode"
+    for fam in ("topk", "stack"):
+        if fam in text:
+            return fam
+    return "decode"
 
 
 def write_stats(args):

@@ -27,7 +27,7 @@ import numpy as np
 BF16_NAN = 0x7FC0
 
 # Purpose codes of the keyed streams.
-_K, _V, _Q, _NEWK, _NEWV, _DIR, _PLANT, _TWIN, _LEN, _VNORM, _NEWVNORM, _HOLES, _SCORES = range(1, 14)
+_K, _V, _Q, _NEWK, _NEWV, _DIR, _PLANT, _TWIN, _LEN, _VNORM, _NEWVNORM, _HOLES, _SCORES, _WQKV, _WO, _X = range(1, 17)
 
 KINDS = ("plain", "sinks", "lognormal_v", "ragged")
 
@@ -271,3 +271,20 @@ def synthetic_scores(B, Hkv, S, seed, kind="ties"):
             raise ValueError(f"unknown score kind {kind!r}")
         out[b] = x
     return out
+
+
+def layer_weights(seed, layer, H, Hq, Hkv, d):
+    """Synthetic projection weights of one attention layer (bf16 bits):
+    w_qkv [(Hq + 2 Hkv) d, H] ~ N(0, 1/H) and w_o [H, Hq d] ~ N(0, 1/(Hq d)),
+    so that activations keep unit scale from layer to layer."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _WQKV, layer, 0])))
+    wq = g.standard_normal(((Hq + 2 * Hkv) * d, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _WO, layer, 0])))
+    wo = g.standard_normal((H, Hq * d), dtype=np.float32) * np.float32(1.0 / np.sqrt(Hq * d))
+    return f32_to_bf16_bits(wq), f32_to_bf16_bits(wo)
+
+
+def token_activations(seed, step, B, H):
+    """bf16 bits [B, H] ~ N(0, 1): the new token's input to the first layer."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _X, step, 0])))
+    return f32_to_bf16_bits(g.standard_normal((B, H), dtype=np.float32))

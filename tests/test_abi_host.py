@@ -3,6 +3,7 @@ declares, and its host-only entry points (shape check, planner, workspace
 size, argument validation) behave as documented.  No kernel is launched."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -17,9 +18,12 @@ HEADER = os.path.join(INCLUDE, "longflow.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    """Every function declared by any header under include/."""
+    names = set()
+    for path in sorted(glob.glob(os.path.join(INCLUDE, "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_every_declared_function_is_exported():
@@ -224,3 +228,68 @@ def test_topk_argument_errors():
     assert _topk_call(out=(1 << 40) + 1024) == lf.LF_E_ALIAS            # inside scores
     assert _topk_call(out=(1 << 40) + (1 << 34) + 8) == lf.LF_E_ALIAS   # inside the mask
     assert _topk_call(B=0, scores=0, mask=0, out=0) == lf.LF_OK
+
+
+def _stack_call(L=2, B=2, H=256, Hq=4, Hkv=2, d=64, S=40, nsplit=1, ws_bytes=None, x_out=None, k1=None,
+                x_in=None, scale=0.125):
+    """longflow_stack_step on fake addresses; only argument errors are asked
+    for, which return before anything is enqueued."""
+    base = 1 << 40
+    step = 1 << 34
+    addr = iter(base + i * step for i in range(64))
+    x_in = next(addr) if x_in is None else x_in
+    xo = next(addr) if x_out is None else x_out
+    pos, ws = next(addr), next(addr)
+    per = {n: [next(addr) for _ in range(L)] for n in ("wq", "wo", "k", "v", "m", "s")}
+    if k1 is not None:
+        per["k"][1] = k1
+    arr = lambda xs: (ctypes.c_void_p * L)(*xs)
+    if ws_bytes is None:
+        ws_bytes = lf.lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, max(nsplit, 1))
+    P = ctypes.c_void_p
+    return lf._lib.longflow_stack_step(L, B, H, Hq, Hkv, d, S, scale, 1e6, P(x_in), P(xo), P(pos), 1,
+                                       arr(per["wq"]), arr(per["wo"]), arr(per["k"]), arr(per["v"]),
+                                       arr(per["m"]), arr(per["s"]), None, P(ws), ws_bytes, nsplit, None), per
+
+
+def test_stack_argument_errors():
+    for kw in ({"L": 0}, {"B": 0}, {"B": 257}, {"H": 96}, {"H": 128}, {"H": 384}, {"Hq": 6, "Hkv": 4}, {"d": 96},
+               {"Hq": 2, "Hkv": 1}):
+        args = dict(kw)
+        assert lf._lib.longflow_stack_step(
+            args.get("L", 2), args.get("B", 2), args.get("H", 256), args.get("Hq", 4), args.get("Hkv", 2),
+            args.get("d", 64), 40, 0.1, 1e6, *([None] * 3), 1, *([None] * 7), None, 0, 1, None) == lf.LF_E_SHAPE, kw
+    assert _stack_call(x_in=0)[0] == lf.LF_E_NULL
+    assert _stack_call(x_in=(1 << 40) + 2)[0] == lf.LF_E_ALIGN
+    assert _stack_call(scale=float("nan"))[0] == lf.LF_E_VALUE
+    assert _stack_call(nsplit=-1)[0] == lf.LF_E_NSPLIT
+    assert _stack_call(ws_bytes=256)[0] == lf.LF_E_WORKSPACE
+
+
+def test_stack_alias_errors():
+    assert _stack_call(x_out=1 << 40)[0] == lf.LF_E_ALIAS            # x_out on x_in
+    rc, per = _stack_call(k1=(1 << 40) + 6 * (1 << 34) + 512)       # layer 1's K inside layer 0's K
+    assert rc == lf.LF_E_ALIAS
+
+
+def test_stack_workspace_size():
+    """The decode workspace first, then qkv, q, k, v, O, two activation
+    buffers, a scores buffer and the projections' split-K partials (fp32, the
+    larger of the two projections), each rounded up to 256 bytes."""
+    up = lambda n: -(-n // 256) * 256
+
+    def ksplit(N, K):  # the projection's K slices: about 256 workgroups of 128 columns, 256-deep
+        blocks, chunks, ks = -(-N // 128), K // 256, 1
+        while ks * 2 <= chunks and chunks % (ks * 2) == 0 and blocks * ks * 2 <= 256:
+            ks *= 2
+        return ks
+
+    for L, B, H, Hq, Hkv, d, S in ((3, 5, 256, 8, 2, 64, 300), (36, 128, 4096, 32, 8, 128, 3200)):
+        nq = (Hq + 2 * Hkv) * d
+        part = max(ksplit(nq, H) * B * nq * 4, ksplit(H, Hq * d) * B * H * 4)
+        for ns in (1, 3):
+            dec = lf.lf_workspace_size(B, Hq, Hkv, d, S, ns)
+            want = up(dec) + up(B * nq * 2) + up(B * Hq * d * 2) + 2 * up(B * Hkv * d * 2) \
+                + up(B * Hq * d * 2) + 2 * up(B * H * 2) + up(B * Hkv * S * 4) + up(part)
+            assert lf.lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, ns) == want
+    assert ksplit(6144, 4096) == 4 and ksplit(4096, 4096) == 8

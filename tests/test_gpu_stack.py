@@ -1,0 +1,232 @@
+"""The multi-layer decode step (include/longflow_stack.h) on the GPU against
+the fp64 oracle (oracle/stack_oracle.py), and its HIP-graph replay against
+eager launches.
+
+Acceptance.  Each stage rounds its output to bf16, as the oracle does, but a
+stage evaluated in fp32 (GPU) and in fp64 (oracle) can round the same value
+to neighbouring bf16 numbers (one ulp, 2^-8 relative) when it lies close to
+a rounding boundary; the next stages then see slightly different inputs.
+Such one-ulp differences enter the residual stream independently at every
+layer, so the gap between the two sides grows like a random walk, about as
+the square root of the depth (measured at the Qwen3-8B shape: score
+differences of 5e-7 at layer 0, 7e-3 at layer 4, 1.4e-2 at layer 16 and at
+most 1.9e-2 by layer 36).  So the stack is held to a looser, depth-scaled
+bound than the single operator, with g(l) = max(1, sqrt(l / 4)) for layer l
+and G = max(1, sqrt(L / 8)) for the whole stack:
+  x_out     |x - x_ref| <= G (3e-2 + 3e-2 |x_ref|) per element, mean <= G 3e-3
+  scores    valid slots within g(l) 1e-2 relative, masked slots exactly +inf
+  evict     equal, or within the oracle's near-tie band widened to g(l) 1e-2
+            relative; both sides then continue from the GPU's choice
+Eager and graph launches run the same kernels in the same order and must
+agree bit for bit.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_05_amd import workloads as W
+from gpu_util import bf16_dev, bf16_host, bf16_value, log
+from oracle.stack_oracle import stack_step
+
+pytestmark = pytest.mark.gpu
+
+X_ATOL = 3e-2
+X_RTOL = 3e-2
+X_MEAN = 3e-3
+SCORE_RTOL = 1e-2
+TIE_RTOL = 1e-2
+BASE = 1e6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from decode_attention_kv_05_amd import longflow  # noqa: F401  (fails loudly if not built)
+    yield
+
+
+def depth_scale(n, per):
+    return max(1.0, float(np.sqrt(n / per)))
+
+
+def evict_ok(gpu, ref_scores, valid, ref, tie):
+    if gpu == ref:
+        return True
+    if ref < 0 or gpu < 0 or not valid[gpu]:
+        return False
+    vals = np.sort(ref_scores[valid])
+    return ref_scores[gpu] <= vals[0] * (1 + tie)
+
+
+class StackCase:
+    """One multi-layer state on the GPU and its oracle copy (host arrays)."""
+
+    def __init__(self, L, B, H, Hq, Hkv, d, S, seed, kind="plain", len_lo=1, nsplit=None, shared_cache=False,
+                 sample=None):
+        from decode_attention_kv_05_amd import longflow as lf
+        self.lf = lf
+        self.L, self.B, self.H, self.Hq, self.Hkv, self.d, self.S = L, B, H, Hq, Hkv, d, S
+        self.seed = seed
+        self.sample = list(range(B)) if sample is None else list(sample)
+        wl = W.Workload(f"stack{seed}", B=B, Hq=Hq, Hkv=Hkv, d=d, S=S, steps=1, kind=kind, seed=seed,
+                        len_lo=len_lo)
+        self.scale = np.float32(1.0 / np.sqrt(d))
+        dev = "cuda"
+        self.layers_ref = []
+        wq, wo, kc, vc, mk, sl, sc = [], [], [], [], [], [], []
+        base_cache = W.initial_cache(wl) if shared_cache else None
+        for l in range(L):
+            k, v, mask = base_cache if shared_cache else W.initial_cache(wl.replace(seed=seed + 17 * l))
+            w1, w2 = W.layer_weights(seed, l, H, Hq, Hkv, d)
+            wq.append(bf16_dev(w1))
+            wo.append(bf16_dev(w2))
+            kc.append(bf16_dev(k))
+            vc.append(bf16_dev(v))
+            mk.append(torch.from_numpy(mask).to(dev))
+            sl.append(torch.full((B, Hkv), -1, dtype=torch.int32, device=dev))
+            sc.append(torch.empty((B, Hkv, S), dtype=torch.float32, device=dev))
+            sb = self.sample
+            self.layers_ref.append({"w_qkv": w1, "w_o": w2, "k": k[sb].copy(), "v": v[sb].copy(),
+                                    "mask": mask[sb].copy(), "slot": np.full((len(sb), Hkv), -1, np.int32)})
+        self.pos_ref = np.array([int(W.valid_length(wl, b)) for b in self.sample], dtype=np.int64)
+        pos_all = np.array([int(W.valid_length(wl, b)) for b in range(B)], dtype=np.int32)
+        self.x_in = torch.empty((B, H), dtype=torch.bfloat16, device=dev)
+        self.x_out = torch.empty((B, H), dtype=torch.bfloat16, device=dev)
+        self.pos = torch.from_numpy(pos_all).to(dev)
+        self.scores = sc
+        self.stack = lf.Stack(self.x_in, self.x_out, self.pos, wq, wo, kc, vc, mk, sl, sc, Hq=Hq,
+                              scale=float(self.scale), rope_base=BASE, nsplit=nsplit)
+        self.t = 0
+
+    def load_token(self, t):
+        x = W.token_activations(self.seed, t, self.B, self.H)
+        self.x_in.copy_(bf16_dev(x))
+        return x
+
+    def check(self, x, where):
+        """Oracle step on the sampled sequences and comparison; lockstep on evict."""
+        sb = self.sample
+        x_ref, trace = stack_step(x[sb], self.pos_ref, self.layers_ref, self.Hq, self.Hkv, self.d, self.scale,
+                                  BASE)
+        xo = bf16_value(bf16_host(self.x_out))[sb]
+        xr = bf16_value(x_ref)
+        err = np.abs(xo - xr)
+        G = depth_scale(self.L, 8)
+        assert np.all(err <= G * (X_ATOL + X_RTOL * np.abs(xr))), f"{where}: x_out max err {err.max():.3e}"
+        assert err.mean() <= G * X_MEAN, f"{where}: x_out mean err {err.mean():.3e}"
+        worst = 0.0
+        exact = total = 0
+        per_layer = []
+        for l in range(self.L):
+            per_layer.append(0.0)
+            s_gpu = self.scores[l].cpu().numpy().astype(np.float64)[sb]
+            slots = self.stack.tensors["slot"][l].cpu().numpy()[sb]
+            s_ref, e_ref = trace[l][5], trace[l][6]
+            g = depth_scale(l, 4)
+            for r in range(len(sb)):
+                valid = self.layers_ref[l]["mask"][r] != 0
+                for j in range(self.Hkv):
+                    assert np.all(np.isposinf(s_gpu[r, j][~valid])), f"{where} l={l}: masked score"
+                    rel = np.abs(s_gpu[r, j][valid] - s_ref[r, j][valid]) / s_ref[r, j][valid]
+                    m = float(rel.max()) if rel.size else 0.0
+                    worst = max(worst, m)
+                    per_layer[-1] = max(per_layer[-1], m)
+                    if not os.environ.get("LF_STACK_DIAG"):
+                        assert np.all(rel <= g * SCORE_RTOL), f"{where} l={l} b={sb[r]} j={j}: score rel {m:.3e}"
+                    assert evict_ok(int(slots[r, j]), s_ref[r, j], valid, int(e_ref[r, j]), g * TIE_RTOL), \
+                        f"{where} l={l} b={sb[r]} j={j}: evict {slots[r, j]} vs {e_ref[r, j]}"
+                    exact += int(slots[r, j]) == int(e_ref[r, j])
+                    total += 1
+            self.layers_ref[l]["slot"][...] = slots  # lockstep on the accepted choice
+        self.pos_ref += 1
+        assert np.array_equal(self.pos.cpu().numpy()[sb], self.pos_ref)
+        log(f"  {where}: x max err {err.max():.2e} mean {err.mean():.2e}; worst score rel {worst:.2e}; "
+            f"evict exact {exact}/{total}")
+        if os.environ.get("LF_STACK_DIAG"):
+            log("  per-layer worst score rel: " + " ".join(f"{v:.1e}" for v in per_layer))
+
+    def run(self, steps, graph=None):
+        for _ in range(steps):
+            x = self.load_token(self.t)
+            if graph is None:
+                self.stack.step()
+            else:
+                graph.launch()
+            torch.cuda.synchronize()
+            self.check(x, f"step {self.t}")
+            self.t += 1
+
+
+@pytest.mark.parametrize("nsplit", [1, 3])
+def test_stack_small_multistep(nsplit):
+    log(f"stack L=3 B=3 H=256 nsplit={nsplit}")
+    case = StackCase(L=3, B=3, H=256, Hq=4, Hkv=2, d=64, S=80, seed=12000, kind="ragged", len_lo=40,
+                     nsplit=nsplit)
+    case.run(4)
+    assert case.lf.lf_read_device_status(case.stack.tensors["workspace"]) == 0
+
+
+@pytest.mark.parametrize("B", [1, 17, 40, 100, 200])
+def test_stack_batch_sizes(B):
+    """Batch sizes that select every row-tile count of the projection kernel."""
+    log(f"stack L=2 B={B}")
+    case = StackCase(L=2, B=B, H=256, Hq=8, Hkv=2, d=128, S=48, seed=12100 + B,
+                     sample=sorted({0, B // 2, B - 1}))
+    case.run(2)
+
+
+def test_stack_gqa8_d64():
+    log("stack GQA 8, d 64")
+    case = StackCase(L=2, B=4, H=512, Hq=16, Hkv=2, d=64, S=300, seed=12200, kind="sinks")
+    case.run(3)
+
+
+def _state(case):
+    t = case.stack.tensors
+    out = [bf16_host(case.x_out), case.pos.cpu().numpy()]
+    for l in range(case.L):
+        out += [bf16_host(t["k_cache"][l]), bf16_host(t["v_cache"][l]), t["slot"][l].cpu().numpy(),
+                case.scores[l].cpu().numpy()]
+    return out
+
+
+def test_stack_graph_replays_match_eager():
+    """Twin states: one stepped with eager launches (and checked against the
+    oracle every step), the other by replaying a graph recorded once, with the
+    new activations copied in between replays; every replay must equal the
+    eager step bit for bit."""
+    log("stack graph vs eager")
+    kw = dict(L=3, B=5, H=256, Hq=8, Hkv=4, d=64, S=120, seed=12300, kind="ragged", len_lo=60, nsplit=2)
+    eager, replay = StackCase(**kw), StackCase(**kw)
+    g = replay.stack.graph()
+    try:
+        for t in range(5):
+            x = eager.load_token(t)
+            eager.stack.step()
+            torch.cuda.synchronize()
+            eager.check(x, f"eager step {t}")
+            replay.load_token(t)
+            g.launch()
+            torch.cuda.synchronize()
+            for a, b in zip(_state(eager), _state(replay)):
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {t} differs"
+    finally:
+        g.close()
+
+
+def test_stack_full_size_qwen3_8b():
+    """36 layers of the Qwen3-8B shape (batch 128, 32/8 heads, d 128, 3200
+    slots, hidden 4096), one step as a graph, sampled sequences against the
+    oracle through all layers."""
+    log("stack full size: generating")
+    case = StackCase(L=36, B=128, H=4096, Hq=32, Hkv=8, d=128, S=3200, seed=12400, shared_cache=True,
+                     sample=[0, 77])
+    g = case.stack.graph()
+    try:
+        case.run(1, graph=g)
+    finally:
+        g.close()
