@@ -47,7 +47,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
-constexpr int kGemmWaves = 8;             // one 16-column slab each
+#ifndef LF_GEMM_WAVES
+#define LF_GEMM_WAVES 8
+#endif
+constexpr int kGemmWaves = LF_GEMM_WAVES;  // one 16-column slab each
 constexpr int kGemmCols = kGemmWaves * 16;  // columns of a workgroup
 constexpr int kGemmChunk = 128;             // k values of A staged per round
 #ifndef LF_GEMM_PAD
