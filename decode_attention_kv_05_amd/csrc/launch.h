@@ -53,9 +53,9 @@ struct GemmParams {
 int gemm_ksplit(int N, int K);
 size_t gemm_partial_bytes(int M, int N, int K);
 
-// qkv [B][(Hq + 2 Hkv) d] -> q [B][Hq][d], k, v [B][Hkv][d]; q and k rotated.
+// The QKV projection's output [B][(Hq + 2 Hkv) d] as q [B][Hq][d], k, v
+// [B][Hkv][d], with q and k rotated (RoPE at pos).
 struct RopeParams {
-  const uint16_t* qkv;
   const int32_t* pos;
   uint16_t* q;
   uint16_t* k;
@@ -66,8 +66,8 @@ struct RopeParams {
 
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
                          hipStream_t stream);
-hipError_t launch_gemm(const GemmParams& prm, hipStream_t stream);
-hipError_t launch_rope_split(const RopeParams& prm, hipStream_t stream);
+// rope set: the epilogue writes q, k, v as RopeParams describes instead of C.
+hipError_t launch_gemm(const GemmParams& prm, hipStream_t stream, const RopeParams* rope = nullptr);
 hipError_t launch_advance_pos(int32_t* pos, int n, hipStream_t stream);
 
 // One decode step after validation (the decode kernel and, for several

@@ -16,10 +16,10 @@
 
 namespace {
 
-constexpr int kMaxStackBatch = 256;  // 16 row tiles of the projection kernel (LDS-staged rows)
+constexpr int kMaxStackBatch = 256;  // two 128-row blocks of the projection kernel
 
 struct StackLayout {
-  size_t dec, qkv, q, k, v, o, x0, x1, scores, part, total;
+  size_t dec, q, k, v, o, x0, x1, scores, part, total;
 };
 
 StackLayout stack_layout(int B, int H, int Hq, int Hkv, int d, int S, size_t dec_bytes) {
@@ -31,7 +31,6 @@ StackLayout stack_layout(int B, int H, int Hq, int Hkv, int d, int S, size_t dec
     return at;
   };
   w.dec = take(dec_bytes);  // first: lf_read_device_status reads its status word
-  w.qkv = take((size_t)B * (Hq + 2 * Hkv) * d * 2);
   w.q = take((size_t)B * Hq * d * 2);
   w.k = take((size_t)B * Hkv * d * 2);
   w.v = take((size_t)B * Hkv * d * 2);
@@ -152,7 +151,6 @@ int enqueue_stack(const StackArgs& a, hipStream_t s) {
   lf_workspace_size(a.B, a.Hq, a.Hkv, a.d, a.S, a.nsplit, &dec_bytes);
   const StackLayout wl = stack_layout(a.B, a.H, a.Hq, a.Hkv, a.d, a.S, dec_bytes);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  uint16_t* qkv = reinterpret_cast<uint16_t*>(ws + wl.qkv);
   uint16_t* q = reinterpret_cast<uint16_t*>(ws + wl.q);
   uint16_t* kn = reinterpret_cast<uint16_t*>(ws + wl.k);
   uint16_t* vn = reinterpret_cast<uint16_t*>(ws + wl.v);
@@ -166,10 +164,9 @@ int enqueue_stack(const StackArgs& a, hipStream_t s) {
   for (int l = 0; l < a.L; ++l) {
     const uint16_t* xin = l == 0 ? static_cast<const uint16_t*>(a.x_in) : xb[(l - 1) & 1];
     uint16_t* xout = l == a.L - 1 ? static_cast<uint16_t*>(a.x_out) : xb[l & 1];
-    lf::GemmParams g1{xin, static_cast<const uint16_t*>(a.w_qkv[l]), nullptr, qkv, part, a.B, nq, a.H, 0, 0};
-    if (lf::launch_gemm(g1, s) != hipSuccess) return LF_E_HIP;
-    lf::RopeParams rp{qkv, a.pos, q, kn, vn, a.B, a.Hq, a.Hkv, a.d, log2_base};
-    if (lf::launch_rope_split(rp, s) != hipSuccess) return LF_E_HIP;
+    lf::GemmParams g1{xin, static_cast<const uint16_t*>(a.w_qkv[l]), nullptr, nullptr, part, a.B, nq, a.H, 0, 0};
+    const lf::RopeParams rp{a.pos, q, kn, vn, a.B, a.Hq, a.Hkv, a.d, log2_base};
+    if (lf::launch_gemm(g1, s, &rp) != hipSuccess) return LF_E_HIP;
     float* sc = (a.scores && a.scores[l]) ? a.scores[l] : ws_scores;
     int rc = lf::enqueue_decode_step(a.B, a.Hq, a.Hkv, a.d, a.S, a.scale, q, a.k_cache[l], a.v_cache[l],
                                      a.mask[l], nullptr, kn, vn, a.slot[l], o, sc, a.slot[l],

@@ -9,22 +9,21 @@
 // ordinary ones of such a module: QKV projection, rotary position embedding
 // of q and the new k, output projection with the residual.
 //
-// gemm_bf16_kernel<MT> + gemm_epilogue_kernel: C[M][N] = A[M][K] W[N][K]^T
+// gemm_bf16_kernel<MT, NCH> + gemm_epilogue_kernel: C[M][N] = A[M][K] W[N][K]^T
 // (+ R[M][N]), bf16 in and out, fp32 accumulation.  At decode M is the batch
-// (at most 16 * MT rows) and the weights are the stream.  A workgroup of 8
-// wavefronts owns 128 columns (a 16-column slab per wave) and one K slice;
-// the slices (split-K, whole 256-deep super-chunks) give about one
-// workgroup per compute unit.  Each 128-deep chunk of A (all rows) is staged
-// once in LDS, double-buffered, and shared by the 8 waves; each wave streams
-// its slab's weights from HBM a 256-deep super-chunk ahead of their use and
-// runs v_mfma_f32_16x16x32_bf16 per 32-deep step and 16-row tile.  Lane l
-// supplies row (or column) l % 16 and the 8 k-values 8 * (l / 16) .. + 7 of
-// both operands and receives column l % 16, rows 4 * (l / 16) .. + 3 of the
-// 16 x 16 result.  The slices' fp32 partials go to a workspace; the epilogue
-// kernel sums them, adds R and rounds to bf16.
+// (up to 128 rows per workgroup; more rows take further row blocks) and the
+// weights are the stream.  A workgroup of 4 wavefronts (one per SIMD) owns
+// 128 columns, two 16-column tiles per wave, and one K slice of NCH 128-deep
+// chunks; the slices (split-K) give about one workgroup per compute unit.
+// v_mfma_f32_16x16x32_bf16 takes, in lane l, row (or column) l % 16 and the
+// 8 k values 8 (l / 16) .. + 7 of each operand's 32-deep step and returns
+// column l % 16, rows 4 (l / 16) .. + 3 of the 16 x 16 result.  The slices'
+// fp32 partials go to a workspace; the epilogue kernel sums them, adds R and
+// rounds to bf16.
 //
-// rope_split_kernel: splits each sequence's qkv row into q [Hq][d],
-// k [Hkv][d] and v [Hkv][d]; q and k pairs (i, i + d/2) are rotated by
+// gemm_rope_epilogue_kernel takes the epilogue's place after the QKV
+// projection: it splits each sequence's qkv row into q [Hq][d], k [Hkv][d]
+// and v [Hkv][d] and rotates the q and k pairs (i, i + d/2) by
 // pos * base^(-2i/d) (angle in fp64, rotation in fp32).
 
 #include <hip/hip_runtime.h>
@@ -37,7 +36,6 @@ namespace lf {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -47,106 +45,128 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
-#ifndef LF_GEMM_WAVES
-#define LF_GEMM_WAVES 8
-#endif
-constexpr int kGemmWaves = LF_GEMM_WAVES;  // one 16-column slab each
-constexpr int kGemmCols = kGemmWaves * 16;  // columns of a workgroup
-constexpr int kGemmChunk = 128;             // k values of A staged per round
-#ifndef LF_GEMM_PAD
-#define LF_GEMM_PAD 8
-#endif
-constexpr int kGemmPad = LF_GEMM_PAD;       // bf16 padding of an LDS row
+constexpr int kGemmWaves = 4;                         // one per SIMD
+constexpr int kGemmNT = 2;                            // 16-column tiles per wave
+constexpr int kGemmCols = kGemmWaves * kGemmNT * 16;  // columns of a workgroup (128)
+constexpr int kGemmChunk = 128;                       // k values per pipeline stage
+constexpr int kGemmSteps = kGemmChunk / 32;           // 32-deep MFMA steps per stage
+static_assert(kGemmSteps == kGemmWaves, "each wave stages one A fragment per row tile");
 
 // Partial products of one K slice: P[ks][m][n] = sum over k in slice ks of
-// A[m][k] W[n][k], for the workgroup's 128 columns and every row of A.
-template <int MT>
+// A[m][k] W[n][k], for the workgroup's 128 columns and rows m0 .. m0 + 16 MT.
+//
+// A stage is one 128-deep chunk of A (all rows), staged in LDS in MFMA
+// fragment order: fragment f = mt * 4 + s (row tile mt, 32-deep step s) is
+// 64 lanes x 16 bytes, lane l holding A[16 mt + l % 16][32 s + 8 (l / 16)
+// .. + 7].  A wave reads or writes a fragment as 1 KB of consecutive LDS,
+// so no access has bank conflicts; each wave stages MT of the stage's 4 MT
+// fragments.  Each wave owns two 16-column tiles, streams their weights
+// from HBM two stages ahead of use, reads the next step's A fragments while
+// the current step multiplies, and reuses every A fragment for both tiles.
+//
+// Per stage j: the loads of A chunk j + 1 and of the weights of chunk j + 2
+// are issued first, then chunk j is multiplied, then A chunk j + 1 goes from
+// registers to LDS; one barrier per stage.  Loads complete in issue order,
+// so that last step waits for A alone and leaves the newest weights in
+// flight.  Every load is unconditional and the chunk loop is unrolled (NCH
+// chunks per slice), so the compiler counts outstanding loads exactly and
+// waits for no more than a step needs.
+template <int MT, int NCH>
 __global__ __launch_bounds__(kGemmWaves * 64) void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __align__(16) uint16_t as[2][MT * 16][kGemmChunk + kGemmPad];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n0 = blockIdx.x * kGemmCols + wave * 16;
-  const bool live = n0 < p.N;  // dead waves still stage A and meet the barriers
+  __shared__ __align__(16) bf16x8_t frag[2][MT * kGemmSteps][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * kGemmCols + wave * (kGemmNT * 16);
   const int col = lane & 15;
   const int kq = (lane >> 4) * 8;
-  const int k_begin = blockIdx.y * p.kslice;
-  const uint16_t* wrow = p.w + (size_t)(live ? n0 + col : 0) * p.K + kq;
+  const int k_begin = blockIdx.y * (NCH * kGemmChunk);
+  const int m0 = blockIdx.z * (MT * 16);  // first row of this row block
 
-  // staging map: thread -> (row, 8 k values) of a 128-deep chunk of A, in
-  // MT * 16 / 32 passes of 32 rows
-  constexpr int kRowsPerPass = kGemmWaves * 64 / (kGemmChunk / 8);  // 32
-  auto stage = [&](int buf, int k0) {
+  // Columns past N read row N - 1 and rows past M repeat row M - 1; their
+  // products are dropped.
+  const uint16_t* wrow[kGemmNT];
 #pragma unroll
-    for (int r0 = 0; r0 < MT * 16; r0 += kRowsPerPass) {
-      const int r = r0 + tid / (kGemmChunk / 8);
-      const int c8 = (tid % (kGemmChunk / 8)) * 8;
-      const uint16_t* src = p.a + (size_t)min(r, p.M - 1) * p.K + k0 + c8;
-      *reinterpret_cast<uint4*>(&as[buf][r][c8]) = *reinterpret_cast<const uint4*>(src);
-    }
-  };
-  constexpr int SPC = kGemmChunk / 32;  // 32-deep steps per A chunk
-  // Weights are loaded a super-chunk (two A chunks, 256 k) at a time: eight
-  // 16-byte loads per lane, issued a whole super-chunk ahead of their use.
-  auto load_w = [&](bf16x8_t (&b)[2 * SPC], int k0) {
+  for (int nt = 0; nt < kGemmNT; ++nt)
+    wrow[nt] = p.w + (size_t)min(n0 + nt * 16 + col, p.N - 1) * p.K + k_begin + kq;
+  // the A fragments this wave stages: f = wave + 4 i, i < MT
+  const uint16_t* arow[MT];
 #pragma unroll
-    for (int s = 0; s < 2 * SPC; ++s)
-      b[s] = live ? *reinterpret_cast<const bf16x8_t*>(wrow + k0 + s * 32) : bf16x8_t{};
-  };
-
-  f32x4_t acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // products of one A chunk (LDS buffer `buf`) with weights b[half * SPC ..]
-  auto compute = [&](const bf16x8_t (&b)[2 * SPC], int half, int buf) {
-#pragma unroll
-    for (int s = 0; s < SPC; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&as[buf][mt * 16 + col][s * 32 + kq]);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[half * SPC + s], acc[mt], 0, 0, 0);
-      }
-    }
-  };
-
-  // A chunk j of the slice lives in LDS buffer j & 1 and is staged while
-  // chunk j - 1 is multiplied.  Super-chunks alternate between two weight
-  // register sets (the loop is unrolled by two super-chunks).
-  constexpr int KS = 2 * kGemmChunk;
-  const int nsuper = p.kslice / KS;
-  bf16x8_t b0[2 * SPC], b1[2 * SPC];
-  load_w(b0, k_begin);
-  stage(0, k_begin);
-  __syncthreads();
-  for (int sc = 0; sc < nsuper; sc += 2) {
-    const int k0 = k_begin + sc * KS;
-    const bool next = sc + 1 < nsuper;
-    if (next) load_w(b1, k0 + KS);
-    stage(1, k0 + kGemmChunk);
-    compute(b0, 0, 0);
-    __syncthreads();
-    if (next) stage(0, k0 + KS);
-    compute(b0, 1, 1);
-    __syncthreads();
-    if (!next) break;
-    const bool next2 = sc + 2 < nsuper;
-    if (next2) load_w(b0, k0 + 2 * KS);
-    stage(1, k0 + KS + kGemmChunk);
-    compute(b1, 0, 0);
-    __syncthreads();
-    if (next2) stage(0, k0 + 2 * KS);
-    compute(b1, 1, 1);
-    __syncthreads();
+  for (int i = 0; i < MT; ++i) {
+    const int f = wave + kGemmWaves * i;
+    const int r = min(m0 + (f / kGemmSteps) * 16 + col, p.M - 1);
+    arow[i] = p.a + (size_t)r * p.K + k_begin + (f % kGemmSteps) * 32 + kq;
   }
-  if (!live) return;
+
+  bf16x8_t w[3][kGemmNT][kGemmSteps];  // chunk c's weights live in w[c % 3]
+  bf16x8_t ar[MT];                      // A fragments of the next chunk
+  auto load_w = [&](int c) {
+#pragma unroll
+    for (int nt = 0; nt < kGemmNT; ++nt)
+#pragma unroll
+      for (int s = 0; s < kGemmSteps; ++s)
+        w[c % 3][nt][s] = *reinterpret_cast<const bf16x8_t*>(wrow[nt] + c * kGemmChunk + s * 32);
+  };
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) ar[i] = *reinterpret_cast<const bf16x8_t*>(arow[i] + c * kGemmChunk);
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) frag[buf][wave + kGemmWaves * i][lane] = ar[i];
+  };
+
+  f32x4_t acc[MT][kGemmNT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kGemmNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load_a(0);
+  load_w(0);
+  if (NCH > 1) load_w(1);
+  store_a(0);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    // the next stage's loads go out before any arithmetic of this one
+    if (j + 1 < NCH) load_a(j + 1);
+    if (j + 2 < NCH) load_w(j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const int buf = j & 1;
+    bf16x8_t af[2][MT];  // A fragments of steps s and s + 1
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) af[0][mt] = frag[buf][mt * kGemmSteps][lane];
+#pragma unroll
+    for (int s = 0; s < kGemmSteps; ++s) {
+      if (s + 1 < kGemmSteps) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) af[(s + 1) & 1][mt] = frag[buf][mt * kGemmSteps + s + 1][lane];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's products
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kGemmNT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s & 1][mt], w[j % 3][nt][s], acc[mt][nt], 0, 0, 0);
+    }
+    if (j + 1 < NCH) {
+      store_a(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
   float* part = p.part + (size_t)blockIdx.y * p.M * p.N;
-  const int n = n0 + col;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int nt = 0; nt < kGemmNT; ++nt) {
+    const int n = n0 + nt * 16 + col;
+    if (n >= p.N) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mt * 16 + (lane >> 4) * 4 + r;
-      if (m < p.M) part[(size_t)m * p.N + n] = acc[mt][r];
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + mt * 16 + (lane >> 4) * 4 + r;
+        if (m < p.M) part[(size_t)m * p.N + n] = acc[mt][nt][r];
+      }
     }
   }
 }
@@ -178,9 +198,15 @@ __global__ void gemm_epilogue_kernel(GemmParams p) {
   }
 }
 
-__global__ void rope_split_kernel(RopeParams p) {
+// The QKV projection's epilogue: sums the K-slice partials of columns
+// h d + i and h d + i + d/2 of head h (i < d/2), rounds them to bf16 (the
+// projection's output precision), rotates the pair by pos * base^(-2i/d)
+// for query and key heads (angle in fp64, rotation in fp32) and writes q, k
+// and v head by head.
+__global__ void gemm_rope_epilogue_kernel(GemmParams g, RopeParams p) {
   const int half = p.d / 2;
   const int heads = p.Hq + 2 * p.Hkv;
+  const size_t plane = (size_t)g.M * g.N;
   const size_t total = (size_t)p.B * heads * half;
   for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
        t += (size_t)gridDim.x * blockDim.x) {
@@ -188,8 +214,13 @@ __global__ void rope_split_kernel(RopeParams p) {
     const size_t bh = t / half;
     const int h = (int)(bh % heads);
     const int b = (int)(bh / heads);
-    const uint16_t* src = p.qkv + ((size_t)b * heads + h) * p.d;
-    const uint16_t x0 = src[i], x1 = src[i + half];
+    const float* src = g.part + (size_t)b * g.N + (size_t)h * p.d + i;
+    float s0 = src[0], s1 = src[half];
+    for (int ks = 1; ks < g.ksplit; ++ks) {
+      s0 += src[ks * plane];
+      s1 += src[ks * plane + half];
+    }
+    const uint16_t x0 = f32_to_bf16_rne(s0), x1 = f32_to_bf16_rne(s1);
     if (h >= p.Hq + p.Hkv) {
       uint16_t* dst = p.v + ((size_t)b * p.Hkv + (h - p.Hq - p.Hkv)) * p.d;
       dst[i] = x0;
@@ -197,9 +228,9 @@ __global__ void rope_split_kernel(RopeParams p) {
       continue;
     }
     const double ang = (double)p.pos[b] * exp2(-(2.0 * i / p.d) * p.log2_base);
-    double s, c;
-    sincos(ang, &s, &c);
-    const float cf = (float)c, sf = (float)s;
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const float cf = (float)cs, sf = (float)sn;
     const float a = bf16_to_f32(x0), bb = bf16_to_f32(x1);
     uint16_t* dst = h < p.Hq ? p.q + ((size_t)b * p.Hq + h) * p.d
                              : p.k + ((size_t)b * p.Hkv + (h - p.Hq)) * p.d;
@@ -221,39 +252,60 @@ __global__ void advance_pos_kernel(int32_t* pos, int n) {
 
 int gemm_ksplit(int N, int K) {
   const int blocks = (N + kGemmCols - 1) / kGemmCols;
-  const int chunks = K / (2 * kGemmChunk);  // slices are whole 256-deep super-chunks
+  const int pieces = K / (2 * kGemmChunk);  // 256-deep pieces; a slice is a whole number of them
+  // the fewest slices of at most 8 pieces (16 chunks, the longest unrolled slice) ...
   int ks = 1;
-  while (ks * 2 <= chunks && chunks % (ks * 2) == 0 && blocks * ks * 2 <= LF_GEMM_TARGET_WG) ks *= 2;
+  while (pieces / ks > 8 || pieces % ks != 0) ++ks;
+  // ... then more slices while the grid stays within the workgroup target
+  for (int c = ks + 1; c <= pieces && blocks * c <= LF_GEMM_TARGET_WG; ++c)
+    if (pieces % c == 0) ks = c;
   return ks;
 }
 
 size_t gemm_partial_bytes(int M, int N, int K) { return (size_t)gemm_ksplit(N, K) * M * N * 4; }
 
-hipError_t launch_gemm(const GemmParams& in, hipStream_t stream) {
+hipError_t launch_gemm(const GemmParams& in, hipStream_t stream, const RopeParams* rope) {
   GemmParams prm = in;
   prm.ksplit = gemm_ksplit(prm.N, prm.K);
   prm.kslice = prm.K / prm.ksplit;
-  const dim3 grid((prm.N + kGemmCols - 1) / kGemmCols, prm.ksplit), block(kGemmWaves * 64);
+  // Up to 128 rows per workgroup; more rows take further row blocks (grid z),
+  // each of which streams the weights again.
   const int tiles = (prm.M + 15) / 16;
-  if (tiles <= 2) hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, block, 0, stream, prm);
-  else if (tiles <= 4) hipLaunchKernelGGL(gemm_bf16_kernel<4>, grid, block, 0, stream, prm);
-  else if (tiles <= 8) hipLaunchKernelGGL(gemm_bf16_kernel<8>, grid, block, 0, stream, prm);
-  else if (tiles <= 16) hipLaunchKernelGGL(gemm_bf16_kernel<16>, grid, block, 0, stream, prm);
-  else return hipErrorInvalidValue;
+  const int mt = tiles <= 2 ? 2 : tiles <= 4 ? 4 : 8;
+  const dim3 grid((prm.N + kGemmCols - 1) / kGemmCols, prm.ksplit, (tiles + mt - 1) / mt);
+  const dim3 block(kGemmWaves * 64);
+  if (prm.M < 1 || grid.z > 65535) return hipErrorInvalidValue;
+  const int nch = prm.kslice / kGemmChunk;  // even, 2 .. 16
+  if (prm.K != prm.ksplit * prm.kslice || nch < 2 || nch > 16 || nch % 2 != 0) return hipErrorInvalidValue;
+#define LF_GEMM_LAUNCH(MT_, NCH_) \
+  case NCH_: hipLaunchKernelGGL((gemm_bf16_kernel<MT_, NCH_>), grid, block, 0, stream, prm); break;
+#define LF_GEMM_BY_NCH(MT_)                                                                  \
+  switch (nch) {                                                                             \
+    LF_GEMM_LAUNCH(MT_, 2) LF_GEMM_LAUNCH(MT_, 4) LF_GEMM_LAUNCH(MT_, 6) LF_GEMM_LAUNCH(MT_, 8) \
+    LF_GEMM_LAUNCH(MT_, 10) LF_GEMM_LAUNCH(MT_, 12) LF_GEMM_LAUNCH(MT_, 14)                    \
+    LF_GEMM_LAUNCH(MT_, 16)                                                                  \
+  }
+  if (mt == 2) {
+    LF_GEMM_BY_NCH(2)
+  } else if (mt == 4) {
+    LF_GEMM_BY_NCH(4)
+  } else {
+    LF_GEMM_BY_NCH(8)
+  }
+#undef LF_GEMM_BY_NCH
+#undef LF_GEMM_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (rope) {
+    const size_t total = (size_t)rope->B * (rope->Hq + 2 * rope->Hkv) * (rope->d / 2);
+    size_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(gemm_rope_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, prm, *rope);
+    return hipGetLastError();
+  }
   size_t blocks = ((size_t)prm.M * prm.N / 4 + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(gemm_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, prm);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope_split(const RopeParams& prm, hipStream_t stream) {
-  const size_t total = (size_t)prm.B * (prm.Hq + 2 * prm.Hkv) * (prm.d / 2);
-  if (total == 0) return hipSuccess;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(rope_split_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 

@@ -273,23 +273,24 @@ def test_stack_alias_errors():
 
 
 def test_stack_workspace_size():
-    """The decode workspace first, then qkv, q, k, v, O, two activation
-    buffers, a scores buffer and the projections' split-K partials (fp32, the
-    larger of the two projections), each rounded up to 256 bytes."""
+    """The decode workspace first, then q, k, v, O, two activation buffers, a
+    scores buffer and the projections' split-K partials (fp32, the larger of
+    the two projections), each rounded up to 256 bytes."""
     up = lambda n: -(-n // 256) * 256
 
-    def ksplit(N, K):  # the projection's K slices: about 256 workgroups of 128 columns, 256-deep
-        blocks, chunks, ks = -(-N // 128), K // 256, 1
-        while ks * 2 <= chunks and chunks % (ks * 2) == 0 and blocks * ks * 2 <= 256:
-            ks *= 2
-        return ks
+    def ksplit(N, K):  # the projection's K slices: whole 256-deep pieces, at most 8 per slice,
+        blocks, pieces = -(-N // 128), K // 256  # then as many as about 256 workgroups of 128 columns allow
+        ks = min(c for c in range(1, pieces + 1) if pieces % c == 0 and pieces // c <= 8)
+        return max(c for c in range(ks, pieces + 1) if pieces % c == 0 and (c == ks or blocks * c <= 256))
 
-    for L, B, H, Hq, Hkv, d, S in ((3, 5, 256, 8, 2, 64, 300), (36, 128, 4096, 32, 8, 128, 3200)):
+    for L, B, H, Hq, Hkv, d, S in ((3, 5, 256, 8, 2, 64, 300), (36, 128, 4096, 32, 8, 128, 3200),
+                                   (2, 200, 5120, 40, 8, 128, 64), (1, 7, 2304, 18, 3, 128, 40)):
         nq = (Hq + 2 * Hkv) * d
         part = max(ksplit(nq, H) * B * nq * 4, ksplit(H, Hq * d) * B * H * 4)
         for ns in (1, 3):
             dec = lf.lf_workspace_size(B, Hq, Hkv, d, S, ns)
-            want = up(dec) + up(B * nq * 2) + up(B * Hq * d * 2) + 2 * up(B * Hkv * d * 2) \
+            want = up(dec) + up(B * Hq * d * 2) + 2 * up(B * Hkv * d * 2) \
                 + up(B * Hq * d * 2) + 2 * up(B * H * 2) + up(B * Hkv * S * 4) + up(part)
             assert lf.lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, ns) == want
     assert ksplit(6144, 4096) == 4 and ksplit(4096, 4096) == 8
+    assert ksplit(7168, 5120) == 4 and ksplit(5120, 5120) == 5 and ksplit(256, 2304) == 9
