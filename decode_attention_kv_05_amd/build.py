@@ -25,7 +25,7 @@ ARCH = "gfx950"
 # headers count for every family).
 _COMMON = ["longflow_api.cpp", "layout.h", "launch.h"]
 _FAMILIES = {"decode": ["longflow_kernels.hip"], "topk": ["evict_topk.hip"],
-             "stack": ["longflow_kernels.hip", "stack_api.cpp", "stack_kernels.hip"]}
+             "stack": ["longflow_kernels.hip", "stack_api.cpp", "stack_kernels.hip", "stack_launch.h"]}
 _HEADERS = {"decode": ["longflow.h"], "topk": ["longflow.h"], "stack": ["longflow.h", "longflow_stack.h"]}
 
 

@@ -38,37 +38,8 @@ struct TopkParams {
   int Hkv, S, k, pairs;
 };
 
-// C[M][N] = A[M][K] W[N][K]^T (+ R[M][N] when r is set), all bf16; part is
-// an fp32 workspace of gemm_partial_bytes(M, N, K) bytes.  N % 16 == 0,
-// K % 256 == 0, M <= 256.
-struct GemmParams {
-  const uint16_t* a;
-  const uint16_t* w;
-  const uint16_t* r;
-  uint16_t* c;
-  float* part;
-  int M, N, K;
-  int ksplit, kslice;  // set by launch_gemm
-};
-int gemm_ksplit(int N, int K);
-size_t gemm_partial_bytes(int M, int N, int K);
-
-// The QKV projection's output [B][(Hq + 2 Hkv) d] as q [B][Hq][d], k, v
-// [B][Hkv][d], with q and k rotated (RoPE at pos).
-struct RopeParams {
-  const int32_t* pos;
-  uint16_t* q;
-  uint16_t* k;
-  uint16_t* v;
-  int B, Hq, Hkv, d;
-  double log2_base;
-};
-
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
                          hipStream_t stream);
-// rope set: the epilogue writes q, k, v as RopeParams describes instead of C.
-hipError_t launch_gemm(const GemmParams& prm, hipStream_t stream, const RopeParams* rope = nullptr);
-hipError_t launch_advance_pos(int32_t* pos, int n, hipStream_t stream);
 
 // One decode step after validation (the decode kernel and, for several
 // splits, the combine and finalize kernels).  mask_w non-null selects the

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "launch.h"
+#include "stack_launch.h"
 #include "layout.h"
 #include "longflow.h"
 #include "longflow_stack.h"

@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "stack_launch.h"
 
 namespace lf {
 
