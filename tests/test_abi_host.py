@@ -294,3 +294,9 @@ def test_stack_workspace_size():
             assert lf.lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, ns) == want
     assert ksplit(6144, 4096) == 4 and ksplit(4096, 4096) == 8
     assert ksplit(7168, 5120) == 4 and ksplit(5120, 5120) == 5 and ksplit(256, 2304) == 9
+    # the GPU stack tests' shapes reach every unrolled slice length (chunks of 128)
+    chunks = set()
+    for H, Hq, Hkv in ((8448, 32, 8), (1280, 48, 8), (3072, 72, 9), (3584, 32, 8), (4096, 32, 8), (256, 4, 2)):
+        nq = (Hq + 2 * Hkv) * 128
+        chunks |= {2 * (H // 256) // ksplit(nq, H), 2 * (Hq * 128 // 256) // ksplit(H, Hq * 128)}
+    assert chunks == {2, 4, 6, 8, 10, 12, 14, 16}

@@ -179,6 +179,20 @@ def test_stack_batch_sizes(B):
     case.run(2)
 
 
+# Shapes whose two projections between them select every K-slice length the
+# projection kernel is unrolled for (2 .. 16 chunks of 128): (QKV, O) =
+# (6, 16), (10, 2), (12, 8), (14, 4) chunks; tests/test_abi_host.py checks
+# the mapping.
+SLICE_SHAPES = [(8448, 32, 8), (1280, 48, 8), (3072, 72, 9), (3584, 32, 8)]
+
+
+@pytest.mark.parametrize("H,Hq,Hkv", SLICE_SHAPES)
+def test_stack_projection_slice_lengths(H, Hq, Hkv):
+    log(f"stack H={H} Hq={Hq} Hkv={Hkv}")
+    case = StackCase(L=1, B=3, H=H, Hq=Hq, Hkv=Hkv, d=128, S=64, seed=12500 + H)
+    case.run(2)
+
+
 def test_stack_gqa8_d64():
     log("stack GQA 8, d 64")
     case = StackCase(L=2, B=4, H=512, Hq=16, Hkv=2, d=64, S=300, seed=12200, kind="sinks")
