@@ -172,7 +172,8 @@ def test_stack_small_multistep(nsplit):
 
 @pytest.mark.parametrize("B", [1, 17, 40, 100, 200])
 def test_stack_batch_sizes(B):
-    """Batch sizes that select every row-tile count of the projection kernel."""
+    """Batch sizes that select each row-tile instantiation of the projection
+    kernel (2, 4 and 8 tiles of 16 rows) and, at 200, two 128-row blocks."""
     log(f"stack L=2 B={B}")
     case = StackCase(L=2, B=B, H=256, Hq=8, Hkv=2, d=128, S=48, seed=12100 + B,
                      sample=sorted({0, B // 2, B - 1}))
