@@ -10,12 +10,14 @@ next evicted slot for every (sequence, KV head), all in one kernel launch.
 The default workload is the Qwen3-8B-shaped layer (batch 128, 32 query / 8
 KV heads, d 128, 3200 slots, bf16 K/V).  Inputs of every step are generated
 and uploaded before timing; the evicted slots go from step to step on the
-device.  Prints one JSON line.
+device.  K steps are timed between one pair of events after W warm-up
+steps; K further steps, each between its own pair of events, give the
+per-launch durations behind the roofline figure.  Prints one JSON line.
 
 Other modes measure the cache-lifecycle entry points on the same shape:
-  fill     longflow_decode_fill on caches that start K + W slots short of
-           full and reach full at the last timed step (the mask grows by one
-           slot per sequence and step)
+  fill     longflow_decode_fill on caches that start 2K + W slots short of
+           full and reach full at the last step (the mask grows by one slot
+           per sequence and step)
   topk     longflow_evict_topk choosing --topk-k slots from synthetic scores
   cadence  longflow_decode with the written slots taken from a top-k queue
            refreshed every --cadence steps (periodic compression)
@@ -184,22 +186,33 @@ def cpu_baseline_fill(wl, max_pairs, fill_from, min_seconds=10.0):
 
 
 def timed(step, K, Wm, stream, dev):
-    """Warm up, then time K steps with one event pair per step on `stream`."""
+    """Warm up with steps 0 .. Wm-1, then time steps Wm .. Wm+K-1 between one
+    pair of events, synchronized on both sides.  Then run steps Wm+K ..
+    Wm+2K-1, untimed as a whole, with an event pair around each for the
+    per-launch durations: events recorded between launches hold the next
+    launch back by a few microseconds, so they stay out of the timed pass.
+    Returns (ms per timed step, per-launch ms of the second pass, wall
+    seconds of the timed pass)."""
     import torch
     for t in range(Wm):
         step(t)
     torch.cuda.synchronize(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
+    start.record(stream)
     for t in range(K):
-        starts[t].record(stream)
         step(Wm + t)
-        ends[t].record(stream)
+    end.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
-    total_ms = starts[0].elapsed_time(ends[-1])
+    total_ms = start.elapsed_time(end)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for t in range(K):
+        starts[t].record(stream)
+        step(Wm + K + t)
+        ends[t].record(stream)
+    torch.cuda.synchronize(dev)
     per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     return total_ms / K, per_launch, wall
 
@@ -281,8 +294,9 @@ def main():
     k, v, mask = W.initial_cache(wl)
     fill_from = None
     if args.mode == "fill":
-        # every sequence starts K + W slots short of full and fills up by the last step
-        fill_from = max(1, wl.S - (K + Wm))
+        # every sequence starts 2K + W slots short of full and fills up by the last step
+        # (W warm-up steps, K timed steps, K steps with per-launch events)
+        fill_from = max(1, wl.S - (2 * K + Wm))
         mask = (np.arange(wl.S)[None, :] < fill_from).astype(np.uint8).repeat(wl.B, 0)
         W.poison_free(k, v, mask)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -334,22 +348,26 @@ def main():
         raise RuntimeError(f"device status flags set during the run: {status:#x}")
 
     if args.mode == "fill":
-        # valid rows of step t (warm-up included): the prefix plus the t + 1 written slots
-        rows = sum(min(wl.S, fill_from + t + 1) for t in range(Wm, Wm + K)) / K
-        kvb = int(rows * wl.B * wl.Hkv * wl.d * 2 * 2)
+        def fill_bytes(t0):
+            # valid rows of step t (warm-up included): the prefix plus the t + 1 written slots
+            rows = sum(min(wl.S, fill_from + t + 1) for t in range(t0, t0 + K)) / K
+            kv = int(rows * wl.B * wl.Hkv * wl.d * 2 * 2)
+            return kv, kv + algorithmic_bytes(wl, np.zeros_like(mask)) + wl.B
+        kvb, algb = fill_bytes(Wm)               # the timed steps
+        _, algb_launch = fill_bytes(Wm + K)      # the steps with per-launch events
         final_mask = dm.cpu().numpy()
-        if not final_mask.all() and fill_from + Wm + K >= wl.S:
+        if not final_mask.all() and fill_from + Wm + 2 * K >= wl.S:
             raise RuntimeError("fill run ended with free slots left")
-        algb = kvb + algorithmic_bytes(wl, np.zeros_like(mask)) + wl.B
     else:
         kvb = kv_bytes(wl, mask)
-        algb = algorithmic_bytes(wl, mask)
+        algb = algb_launch = algorithmic_bytes(wl, mask)
+    # step index of the per-launch durations: Wm + K + t
     if args.mode == "cadence":
         # decode launches only: top-k launches are timed inside the steps that run them
-        dec = np.array([x for t, x in enumerate(per_launch) if (Wm + t + 1) % N != 0])
+        dec = np.array([x for t, x in enumerate(per_launch) if (Wm + K + t + 1) % N != 0])
         rl = roofline(algb, dec if dec.size else per_launch, "longflow_decode_kernel", None)
     else:
-        rl = roofline(algb, per_launch, "longflow_decode_kernel",
+        rl = roofline(algb_launch, per_launch, "longflow_decode_kernel",
                       measured_traffic(f"{wl.name}/nsplit{nsplit}" + ("/fill" if args.mode == "fill" else "")))
     metric = {
         "decode": METRIC,
@@ -386,7 +404,7 @@ def main():
         result["config"].update({"mode": "fill", "start_valid_slots": fill_from})
     if args.mode == "cadence":
         result["config"].update({"mode": "cadence", "cadence": N})
-        refresh = [x for t, x in enumerate(per_launch) if (Wm + t + 1) % N == 0]
+        refresh = [x for t, x in enumerate(per_launch) if (Wm + K + t + 1) % N == 0]
         if refresh:
             result["refresh_step_us_mean"] = round(float(np.mean(refresh)) * 1e3, 2)
     if not args.no_cpu_baseline and args.mode != "cadence":
