@@ -17,9 +17,11 @@
 //   keys    scores and mask bytes are loaded eight per thread at a time, all
 //           issued before any is used; rows of up to kStageSlots slots keep
 //           their keys in LDS, longer rows re-read them from memory.
-//   select  four 8-bit radix passes (LDS histogram, block prefix sum) find
-//           the key T of the k-th smallest valid slot and how many slots with
-//           key T are still needed ("need").
+//   select  three radix passes over 11, 11 and 10 key bits (LDS histogram,
+//           block prefix sum) find the key T of the k-th smallest valid slot
+//           and how many slots with key T are still needed ("need").  Scores
+//           cluster in a few exponents, so an 8-bit top digit would send most
+//           atomics of the first pass to a handful of bins.
 //   compact each wave owns a contiguous, 64-aligned run of slots: a counting
 //           pass gives every wave its output offset (one barrier), then each
 //           wave places its slots with key < T, and the first `need` slots
@@ -39,6 +41,10 @@ constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkBatch = 8;       // slots loaded per thread before use
 constexpr int kStageSlots = 16384;  // keys staged in LDS (64 KB) up to this row length
 constexpr uint32_t kInvalidKey = 0xffffffffu;
+constexpr int kRadixPasses = 3;
+constexpr int kBinsMax = 2048;  // 11-bit digits
+__host__ __device__ constexpr int radix_bits(int pass) { return pass < 2 ? 11 : 10; }
+__host__ __device__ constexpr int radix_shift(int pass) { return pass == 0 ? 21 : pass == 1 ? 10 : 0; }
 
 __device__ __forceinline__ uint32_t value_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -91,7 +97,7 @@ __device__ __forceinline__ uint32_t block_exclusive(uint32_t x, uint32_t* wtot, 
 template <bool STAGE>
 __global__ __launch_bounds__(kTopkThreads) void evict_topk_kernel(TopkParams p) {
   extern __shared__ uint32_t keys[];  // [S] when STAGE
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kBinsMax];
   __shared__ uint32_t wtot[kTopkWaves];
   __shared__ uint32_t wcount[2][kTopkWaves];
   __shared__ uint32_t pick[2];
@@ -109,8 +115,8 @@ __global__ __launch_bounds__(kTopkThreads) void evict_topk_kernel(TopkParams p) 
   const float* srow = p.scores + (size_t)pair * S;
   const uint8_t* mrow = p.mask + (size_t)b * S;
 
-  // ---- keys, valid count and the histogram of the top byte
-  hist[tid] = 0;
+  // ---- keys, valid count and the histogram of the top 11 bits
+  for (int i = tid; i < kBinsMax; i += kTopkThreads) hist[i] = 0;
   __syncthreads();
   uint32_t nvalid = 0;
   for (int base = 0; base < S; base += kTopkBatch * kTopkThreads) {
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kTopkThreads) void evict_topk_kernel(TopkParams p) 
       if (STAGE && i < S) keys[i] = key[u];
       if (key[u] != kInvalidKey) {
         ++nvalid;
-        atomicAdd(&hist[key[u] >> 24], 1u);
+        atomicAdd(&hist[key[u] >> radix_shift(0)], 1u);
       }
     }
   }
@@ -133,12 +139,14 @@ __global__ __launch_bounds__(kTopkThreads) void evict_topk_kernel(TopkParams p) 
   uint32_t need = (uint32_t)p.k;
   if (nvalid > (uint32_t)p.k) {
     uint32_t prefix = 0, krem = (uint32_t)p.k;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    for (int pass = 0; pass < kRadixPasses; ++pass) {
+      const int shift = radix_shift(pass);
+      const int nb = 1 << radix_bits(pass);
       if (pass > 0) {
-        hist[tid] = 0;
+        for (int i = tid; i < kBinsMax; i += kTopkThreads) hist[i] = 0;
         __syncthreads();
-        const uint32_t hi_mask = ~0u << (shift + 8);
+        const uint32_t hi_mask = ~0u << (shift + radix_bits(pass));
+        const uint32_t dmask = (uint32_t)nb - 1u;
         if (STAGE) {
           // eight LDS reads in flight before the first update
           for (int base = 0; base < S; base += kTopkBatch * kTopkThreads) {
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(kTopkThreads) void evict_topk_kernel(TopkParams p) 
 #pragma unroll
             for (int u = 0; u < kTopkBatch; ++u)
               if (key[u] != kInvalidKey && (key[u] & hi_mask) == prefix)
-                atomicAdd(&hist[(key[u] >> shift) & 255u], 1u);
+                atomicAdd(&hist[(key[u] >> shift) & dmask], 1u);
           }
         } else {
           for (int base = 0; base < S; base += kTopkBatch * kTopkThreads) {
@@ -160,18 +168,30 @@ __global__ __launch_bounds__(kTopkThreads) void evict_topk_kernel(TopkParams p) 
 #pragma unroll
             for (int u = 0; u < kTopkBatch; ++u)
               if (key[u] != kInvalidKey && (key[u] & hi_mask) == prefix)
-                atomicAdd(&hist[(key[u] >> shift) & 255u], 1u);
+                atomicAdd(&hist[(key[u] >> shift) & dmask], 1u);
           }
         }
         __syncthreads();
       }
-      // the digit whose bin holds the krem-th smallest of the remaining keys
-      const uint32_t h = hist[tid];
+      // the digit whose bin holds the krem-th smallest of the remaining keys:
+      // thread t owns nb / 256 consecutive bins
+      const int per = nb / kTopkThreads;
+      uint32_t h[kBinsMax / kTopkThreads];
+      uint32_t mine = 0;
+#pragma unroll
+      for (int q = 0; q < kBinsMax / kTopkThreads; ++q) {
+        h[q] = q < per ? hist[tid * per + q] : 0u;
+        mine += h[q];
+      }
       uint32_t excl;
-      block_exclusive(h, wtot, excl);
-      if (excl < krem && krem <= excl + h) {
-        pick[0] = (uint32_t)tid;
-        pick[1] = krem - excl;
+      block_exclusive(mine, wtot, excl);
+#pragma unroll
+      for (int q = 0; q < kBinsMax / kTopkThreads; ++q) {
+        if (q < per && excl < krem && krem <= excl + h[q]) {
+          pick[0] = (uint32_t)(tid * per + q);
+          pick[1] = krem - excl;
+        }
+        if (q < per) excl += h[q];
       }
       __syncthreads();
       prefix |= pick[0] << shift;
