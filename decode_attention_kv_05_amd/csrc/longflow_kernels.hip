@@ -678,14 +678,64 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
   const int nsplit = p.nsplit;
   const float* ml = p.part_ml + (size_t)pair * nsplit * GP * 2;
 
+  const size_t row0 = (size_t)pair * p.S;
+  const float* wl = p.ws_logit + row0 * GP;
+  const float* wv = p.ws_vnorm + row0;
+  const uint8_t* mrow = p.mask + (size_t)b * p.S;
+  float* sr = p.scores + row0;
+  const int base = chunk * kCombineRows;
+  // Every load is issued, mask, logits and |v|_1 together, before any is
+  // used (rows past S read row S - 1); the mask only decides what the values
+  // are used for.  A masked row's workspace entry may be stale and is never
+  // used.
+  bool valid[R];
+  uint8_t mk[R];
+  float vn[R];
+  float s[R][GP];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int r = min(base + u * kCombineThreads + tid, p.S - 1);
+    mk[u] = mrow[r];
+    vn[u] = wv[r];
+    if constexpr (GP >= 4) {
+#pragma unroll
+      for (int h4 = 0; h4 < GP; h4 += 4) {
+        const float4 x = reinterpret_cast<const float4*>(wl + (size_t)r * GP + h4)[0];
+        s[u][h4] = x.x;
+        s[u][h4 + 1] = x.y;
+        s[u][h4 + 2] = x.z;
+        s[u][h4 + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < GP; ++h) s[u][h] = wl[(size_t)r * GP + h];
+    }
+  }
+  // The pair's global max M_h and sum L_h over the splits, split partials
+  // read eight at a time (the order of the sums is the split order).
   if (tid < GP) {
+    constexpr int SB = 8;
     float m = kNegInf;
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, ml[(s * GP + tid) * 2]);
+    for (int s0 = 0; s0 < nsplit; s0 += SB) {
+      float ms[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) ms[u] = ml[(min(s0 + u, nsplit - 1) * GP + tid) * 2];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) m = s0 + u < nsplit ? fmaxf(m, ms[u]) : m;
+    }
     float l = 0.f;
     if (m != kNegInf) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float ms = ml[(s * GP + tid) * 2];
-        if (ms != kNegInf) l += ml[(s * GP + tid) * 2 + 1] * exp2f(ms - m);
+      for (int s0 = 0; s0 < nsplit; s0 += SB) {
+        float ms[SB], ls[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int sc = min(s0 + u, nsplit - 1);
+          ms[u] = ml[(sc * GP + tid) * 2];
+          ls[u] = ml[(sc * GP + tid) * 2 + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+          if (s0 + u < nsplit && ms[u] != kNegInf) l += ls[u] * exp2f(ms[u] - m);
       }
     }
     stat_m[tid] = m;
@@ -695,15 +745,24 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
 
   if (chunk == 0) {
     const float* po = p.part_o + (size_t)pair * nsplit * GP * D;
+    constexpr int SB = 4;
     for (int idx = tid; idx < GP * D; idx += kCombineThreads) {
       const int h = idx / D;
       if (h >= p.G) continue;
       const float m = stat_m[h];
       float o = 0.f;
       if (m != kNegInf) {
-        for (int s = 0; s < nsplit; ++s) {
-          const float ms = ml[(s * GP + h) * 2];
-          if (ms != kNegInf) o += po[(size_t)s * GP * D + idx] * exp2f(ms - m);
+        for (int s0 = 0; s0 < nsplit; s0 += SB) {
+          float pv[SB], ms[SB];
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            const int sc = min(s0 + u, nsplit - 1);
+            pv[u] = po[(size_t)sc * GP * D + idx];
+            ms[u] = ml[(sc * GP + h) * 2];
+          }
+#pragma unroll
+          for (int u = 0; u < SB; ++u)
+            if (s0 + u < nsplit && ms[u] != kNegInf) o += pv[u] * exp2f(ms[u] - m);
         }
       }
       p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] =
@@ -717,39 +776,8 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
     gm[h] = stat_m[h];
     gil[h] = h < p.G ? stat_il[h] : 0.f;
   }
-  const size_t row0 = (size_t)pair * p.S;
-  const float* wl = p.ws_logit + row0 * GP;
-  const float* wv = p.ws_vnorm + row0;
-  const uint8_t* mrow = p.mask + (size_t)b * p.S;
-  float* sr = p.scores + row0;
-  const int base = chunk * kCombineRows;
-  bool valid[R];
-  float vn[R];
-  float s[R][GP];
 #pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int r = base + u * kCombineThreads + tid;
-    valid[u] = r < p.S && mrow[r] != 0;
-  }
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int r = base + u * kCombineThreads + tid;
-    vn[u] = valid[u] ? wv[r] : 0.f;
-    if constexpr (GP >= 4) {
-#pragma unroll
-      for (int h4 = 0; h4 < GP; h4 += 4) {
-        const float4 x = valid[u] ? reinterpret_cast<const float4*>(wl + (size_t)r * GP + h4)[0]
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-        s[u][h4] = x.x;
-        s[u][h4 + 1] = x.y;
-        s[u][h4 + 2] = x.z;
-        s[u][h4 + 3] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < GP; ++h) s[u][h] = valid[u] ? wl[(size_t)r * GP + h] : 0.f;
-    }
-  }
+  for (int u = 0; u < R; ++u) valid[u] = base + u * kCombineThreads + tid < p.S && mk[u] != 0;
   // Fill step: the lowest free slot of the chunk.  The decode kernel has
   // already added the written slots to the mask.
   if (p.fill) {
