@@ -54,7 +54,7 @@ def compare_pair(o_gpu, s_gpu, e_gpu, o_ref, s_ref, e_ref, valid, where):
     """Assert the acceptance rule for one (b, j); returns True at an exact evict match."""
     err = np.abs(o_gpu - o_ref)
     tol = O_ATOL + O_RTOL * np.abs(o_ref)
-    assert np.all(err <= tol), f"{where}: O max err {err.max():.3e} (tol {tol[np.argmax(err - tol)]:.3e})"
+    assert np.all(err <= tol), f"{where}: O max err {err.max():.3e} (tol {tol.flat[np.argmax(err - tol)]:.3e})"
     assert np.all(np.isposinf(s_gpu[~valid])), f"{where}: masked scores not +inf"
     sv, rv = s_gpu[valid], s_ref[valid]
     rel = np.abs(sv - rv) / np.maximum(rv, 1e-300)

@@ -1,0 +1,93 @@
+"""Randomised parity cases for the operator and the k-slot selection.
+
+The cases are drawn once from a fixed seed, so every run checks the same
+list; they combine what the hand-written cases vary one at a time: group size
+(1..8, padded ones included), head count, d, slot counts from 1 to a few
+thousand, the workload kinds, masks with scattered holes and explicit split
+counts.  Holed masks go over the caches of the kinds without a valid-length
+prefix (every slot holds finite data), and the K/V of their free slots are
+poisoned with NaN.  Each decode case runs three steps in lockstep with the
+oracle and checks the written cache rows; each selection case compares the k
+slots bit for bit.  Acceptance is the operator's (tests/gpu_util.py)."""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_05_amd import workloads as W
+from gpu_util import Lockstep, log
+from oracle import evict_topk
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_cases():
+    rng = np.random.default_rng(20261202)
+    cases = []
+    for i in range(24):
+        G = int(rng.integers(1, 9))
+        Hkv = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 5))
+        S = max(1, int(np.exp(rng.uniform(0.0, np.log(2500.0)))))
+        kind = str(rng.choice(W.KINDS))
+        holes = float(rng.choice([0.0, 0.0, 0.5, 0.9, 0.02]))  # 0: the kind's own mask
+        if holes and kind == "ragged":
+            kind = "plain"  # the ragged kind's cache is NaN past each valid length
+        ns = int(rng.choice([0, 1, 2, 3, 5, 8]))
+        nsplit = min(ns, S) if ns else None  # None: the library's plan
+        cases.append((i, B, G, Hkv, d, S, kind, holes, nsplit))
+    return cases
+
+
+def _topk_cases():
+    rng = np.random.default_rng(20261203)
+    cases = []
+    for i in range(16):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.integers(1, 5))
+        S = max(1, int(np.exp(rng.uniform(0.0, np.log(20000.0)))))
+        k = int(rng.integers(1, S + 1))
+        kind = str(rng.choice(["ties", "spread", "special"]))
+        frac = float(rng.choice([1.0, 0.7, 0.1, 0.0]))
+        cases.append((i, B, Hkv, S, k, kind, frac))
+    return cases
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from decode_attention_kv_05_amd import longflow  # noqa: F401  (fails loudly if not built)
+    yield
+
+
+@pytest.mark.parametrize("case", _decode_cases(), ids=lambda c: f"r{c[0]}")
+def test_random_decode_lockstep(case):
+    i, B, G, Hkv, d, S, kind, holes, nsplit = case
+    log(f"random decode {i}: B={B} G={G} Hkv={Hkv} d={d} S={S} {kind} holes={holes} nsplit={nsplit}")
+    wl = W.Workload(f"rand{i}", B=B, Hq=G * Hkv, Hkv=Hkv, d=d, S=S, steps=3, kind=kind, seed=31000 + i,
+                    len_lo=min(S, 1 + S // 4))
+    k, v, mask = W.initial_cache(wl)
+    if holes:
+        mask = W.holed_mask(wl, 1.0 - holes)
+        if B > 1:
+            mask[B - 1] = 0  # a sequence with no valid slot
+        W.poison_free(k, v, mask)
+    ls = Lockstep(wl, nsplit=nsplit, state=(k, v, mask))
+    for _ in range(wl.steps):
+        ls.step()
+    ls.check_full_cache()
+
+
+@pytest.mark.parametrize("case", _topk_cases(), ids=lambda c: f"t{c[0]}")
+def test_random_topk_exact(case):
+    i, B, Hkv, S, k, kind, frac = case
+    log(f"random top-k {i}: B={B} Hkv={Hkv} S={S} k={k} {kind} valid={frac}")
+    from decode_attention_kv_05_amd import longflow as lf
+    scores = W.synthetic_scores(B, Hkv, S, seed=32000 + i, kind=kind)
+    mask = (np.random.default_rng(33000 + i).random((B, S)) < frac).astype(np.uint8)
+    got = lf.longflow_evict_topk(torch.from_numpy(scores).cuda(), torch.from_numpy(mask).cuda(), k)
+    torch.cuda.synchronize()
+    want = evict_topk(scores, (mask != 0)[:, None, :], k)  # [B, Hkv, k]
+    assert np.array_equal(got.cpu().numpy(), np.moveaxis(want, -1, 0))
