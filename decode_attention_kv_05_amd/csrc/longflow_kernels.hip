@@ -481,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
       float l = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) l += red[w * GP + tid];
-      stat_il[tid] = l > 0.f ? 1.0f / l : 0.f;
+      stat_il[tid] = (l > 0.f || l != l) ? 1.0f / l : 0.f;  // NaN logits make every p NaN
       if (SPLIT) {
         float* ml = p.part_ml + (((size_t)pair * nsplit + sp) * GP + tid) * 2;
         ml[0] = stat_m[tid];
@@ -723,23 +723,24 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
 #pragma unroll
       for (int u = 0; u < SB; ++u) m = s0 + u < nsplit ? fmaxf(m, ms[u]) : m;
     }
+    // A split without a finite logit adds its sum as it is: 0 when it has no
+    // valid slot, NaN when its valid logits are NaN, which then reaches O and
+    // the scores as it does with one split.
     float l = 0.f;
-    if (m != kNegInf) {
-      for (int s0 = 0; s0 < nsplit; s0 += SB) {
-        float ms[SB], ls[SB];
+    for (int s0 = 0; s0 < nsplit; s0 += SB) {
+      float ms[SB], ls[SB];
 #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int sc = min(s0 + u, nsplit - 1);
-          ms[u] = ml[(sc * GP + tid) * 2];
-          ls[u] = ml[(sc * GP + tid) * 2 + 1];
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u)
-          if (s0 + u < nsplit && ms[u] != kNegInf) l += ls[u] * exp2f(ms[u] - m);
+      for (int u = 0; u < SB; ++u) {
+        const int sc = min(s0 + u, nsplit - 1);
+        ms[u] = ml[(sc * GP + tid) * 2];
+        ls[u] = ml[(sc * GP + tid) * 2 + 1];
       }
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        if (s0 + u < nsplit) l += ms[u] != kNegInf ? ls[u] * exp2f(ms[u] - m) : ls[u];
     }
     stat_m[tid] = m;
-    stat_il[tid] = l > 0.f ? 1.0f / l : 0.f;
+    stat_il[tid] = (l > 0.f || l != l) ? 1.0f / l : 0.f;
   }
   __syncthreads();
 

@@ -131,6 +131,33 @@ def test_prev_slot_status_flags(nsplit):
     assert lf.lf_read_device_status(ws) == 0
 
 
+def test_nan_in_valid_slots_same_for_every_split_count():
+    """NaN in valid K rows is not checked, but it reaches O and the scores the
+    same way whatever the split count: a pair whose valid keys are all NaN,
+    a pair with one NaN key row, and untouched pairs."""
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("nan", B=2, Hq=4, Hkv=2, d=64, S=64, steps=1, seed=44)
+    k, v, mask = W.initial_cache(wl)
+    k[0, 0, :] = W.BF16_NAN        # every valid key of pair (0, 0)
+    k[1, 1, 10] = W.BF16_NAN       # one key of pair (1, 1)
+    q, nk, nv = W.step_inputs(wl, 0)
+    prev = torch.full((wl.B, wl.Hkv), -1, dtype=torch.int32, device="cuda")
+    res = []
+    for nsplit in (1, 4):
+        log(f"NaN keys, nsplit={nsplit}")
+        out, sc, ev = lf.longflow_decode(bf16_dev(q), bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda(),
+                                         bf16_dev(nk), bf16_dev(nv), prev, nsplit=nsplit)
+        torch.cuda.synchronize()
+        res.append((bf16_value(bf16_host(out)), sc.cpu().numpy()))
+    (o1, s1), (o4, s4) = res
+    assert np.array_equal(np.isnan(o1), np.isnan(o4)) and np.array_equal(np.isnan(s1), np.isnan(s4))
+    assert np.isnan(o1[0, 0:2]).all() and np.isnan(o1[1, 2:4]).all()
+    assert not np.isnan(o1[0, 2:4]).any() and not np.isnan(o1[1, 0:2]).any()
+    assert np.isnan(s1[0, 0]).all() and not np.isnan(s1[0, 1]).any()
+    fin = ~np.isnan(o1)
+    assert np.allclose(o1[fin], o4[fin], rtol=1e-2, atol=1e-2)
+
+
 def test_empty_batch_is_a_no_op():
     from decode_attention_kv_05_amd import longflow as lf
     e = lambda *s, dt=torch.bfloat16: torch.empty(s, dtype=dt, device="cuda")
