@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from decode_attention_kv_05_amd import workloads as W
-from gpu_util import TIE_RTOL, bf16_dev, bf16_host, bf16_value, compare_pair, log
+from gpu_util import TIE_RTOL, FillLockstep, bf16_dev, bf16_host, bf16_value, compare_pair, log, lowest_free
 from oracle import decode_step, decode_step_fill, evict_topk
 
 pytestmark = pytest.mark.gpu
@@ -32,79 +32,6 @@ def _device():
 def _lf():
     from decode_attention_kv_05_amd import longflow as lf
     return lf
-
-
-def lowest_free(mask):
-    """First free slot of each sequence, -1 for a full one."""
-    free = mask == 0
-    return np.where(free.any(axis=1), free.argmax(axis=1), -1).astype(np.int32)
-
-
-class FillLockstep:
-    """Fill steps on the GPU and in the oracle from the same state; both sides
-    continue from the GPU's next slot once it has been accepted."""
-
-    def __init__(self, wl, k, v, mask, prev, nsplit=None):
-        lf = _lf()
-        self.lf, self.wl, self.nsplit = lf, wl, nsplit
-        self.k_ref, self.v_ref, self.mask = k, v, mask.copy()
-        self.dk, self.dv = bf16_dev(k), bf16_dev(v)
-        self.dm = torch.from_numpy(mask.copy()).cuda()
-        self.prev = prev.astype(np.int32)
-        self.dprev = torch.from_numpy(self.prev.copy()).cuda()
-        self.ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, nsplit)
-        self.t = 0
-        self.exact = self.total = 0
-        self.last = None
-
-    def step(self, use_fill=True):
-        wl, t = self.wl, self.t
-        q, nk, nv = W.step_inputs(wl, t)
-        entry = self.lf.longflow_decode_fill if use_fill else self.lf.longflow_decode
-        out, sc, nx = entry(bf16_dev(q), self.dk, self.dv, self.dm, bf16_dev(nk), bf16_dev(nv), self.dprev,
-                            scale=float(wl.scale), workspace=self.ws, nsplit=self.nsplit)
-        torch.cuda.synchronize()
-        if use_fill:
-            o_ref, s_ref, n_ref, m_ref = decode_step_fill(q, self.k_ref, self.v_ref, self.mask, nk, nv,
-                                                          self.prev, wl.scale)
-        else:
-            o_ref, s_ref, n_ref = decode_step(q, self.k_ref, self.v_ref, self.mask, nk, nv, self.prev, wl.scale)
-            m_ref = self.mask
-        m_gpu = self.dm.cpu().numpy()
-        assert np.array_equal(m_gpu, m_ref), f"{wl.name} t={t}: mask differs"
-        o_gpu = bf16_value(bf16_host(out))
-        s_gpu = sc.cpu().numpy().astype(np.float64)
-        n_gpu = nx.cpu().numpy()
-        for b in range(wl.B):
-            has_free = bool((m_ref[b] == 0).any())
-            valid = m_ref[b] != 0
-            for j in range(wl.Hkv):
-                where = f"{wl.name} t={t} b={b} j={j}"
-                if use_fill and has_free:
-                    assert n_gpu[b, j] == n_ref[b, j], f"{where}: next slot {n_gpu[b, j]} != {n_ref[b, j]}"
-                heads = slice(j * wl.G, (j + 1) * wl.G)
-                self.exact += compare_pair(o_gpu[b, heads], s_gpu[b, j], n_gpu[b, j], o_ref[b, heads],
-                                           s_ref[b, j], n_ref[b, j], valid, where)
-                self.total += 1
-                p = int(self.prev[b, j])
-                if p >= 0:
-                    assert np.array_equal(bf16_host(self.dk[b, j, p]), nk[b, j]), where
-                    assert np.array_equal(bf16_host(self.dv[b, j, p]), nv[b, j]), where
-        self.mask = m_ref.copy()
-        self.prev = n_gpu.astype(np.int32)
-        self.dprev = nx.clone()
-        self.last = (sc, s_ref)
-        self.t += 1
-        return out, sc, nx
-
-    def finish(self):
-        assert self.lf.lf_read_device_status(self.ws) == 0
-        for b in range(self.wl.B):
-            for j in range(self.wl.Hkv):
-                valid = self.mask[b] != 0
-                assert np.array_equal(bf16_host(self.dk[b, j])[valid], self.k_ref[b, j][valid])
-                assert np.array_equal(bf16_host(self.dv[b, j])[valid], self.v_ref[b, j][valid])
-        log(f"  {self.wl.name}: {self.t} steps, next slot exact {self.exact}/{self.total}")
 
 
 @pytest.mark.parametrize("nsplit", [1, 3])

@@ -1,4 +1,5 @@
-"""Randomised parity cases for the operator and the k-slot selection.
+"""Randomised parity cases for the operator, the fill step and the k-slot
+selection.
 
 The cases are drawn once from a fixed seed, so every run checks the same
 list; they combine what the hand-written cases vary one at a time: group size
@@ -7,15 +8,17 @@ thousand, the workload kinds, masks with scattered holes and explicit split
 counts.  Holed masks go over the caches of the kinds without a valid-length
 prefix (every slot holds finite data), and the K/V of their free slots are
 poisoned with NaN.  Each decode case runs three steps in lockstep with the
-oracle and checks the written cache rows; each selection case compares the k
-slots bit for bit.  Acceptance is the operator's (tests/gpu_util.py)."""
+oracle and checks the written cache rows; each fill case fills its caches
+through to eviction in lockstep, the mask and every free-slot choice exact;
+each selection case compares the k slots bit for bit.  Acceptance is the
+operator's (tests/gpu_util.py)."""
 
 import numpy as np
 import pytest
 import torch
 
 from decode_attention_kv_05_amd import workloads as W
-from gpu_util import Lockstep, log
+from gpu_util import FillLockstep, Lockstep, log, lowest_free
 from oracle import evict_topk
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +27,7 @@ pytestmark = pytest.mark.gpu
 def _decode_cases():
     rng = np.random.default_rng(20261202)
     cases = []
-    for i in range(24):
+    for i in range(48):
         G = int(rng.integers(1, 9))
         Hkv = int(rng.integers(1, 4))
         d = int(rng.choice([64, 128]))
@@ -40,10 +43,26 @@ def _decode_cases():
     return cases
 
 
+def _fill_cases():
+    rng = np.random.default_rng(20261204)
+    cases = []
+    for i in range(16):
+        G = int(rng.integers(1, 9))
+        Hkv = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 4))
+        S = int(rng.integers(2, 600))
+        free = int(rng.integers(1, min(S, 30) + 1))  # free slots per sequence, about
+        ns = int(rng.choice([0, 1, 2, 3, 5]))
+        nsplit = min(ns, S) if ns else None
+        cases.append((i, B, G, Hkv, d, S, free, nsplit))
+    return cases
+
+
 def _topk_cases():
     rng = np.random.default_rng(20261203)
     cases = []
-    for i in range(16):
+    for i in range(32):
         B = int(rng.integers(1, 4))
         Hkv = int(rng.integers(1, 5))
         S = max(1, int(np.exp(rng.uniform(0.0, np.log(20000.0)))))
@@ -78,6 +97,26 @@ def test_random_decode_lockstep(case):
     for _ in range(wl.steps):
         ls.step()
     ls.check_full_cache()
+
+
+@pytest.mark.parametrize("case", _fill_cases(), ids=lambda c: f"f{c[0]}")
+def test_random_fill_lockstep(case):
+    """Free slots scattered through the cache (the first sequence may start
+    with nothing to write); fill steps until every cache is full, then two
+    more, in lockstep with the oracle."""
+    i, B, G, Hkv, d, S, free, nsplit = case
+    log(f"random fill {i}: B={B} G={G} Hkv={Hkv} d={d} S={S} free~{free} nsplit={nsplit}")
+    wl = W.Workload(f"rfill{i}", B=B, Hq=G * Hkv, Hkv=Hkv, d=d, S=S, steps=1, kind="plain", seed=34000 + i)
+    k, v, _ = W.initial_cache(wl)
+    mask = W.holed_mask(wl, 1.0 - free / S)
+    W.poison_free(k, v, mask)
+    prev = np.repeat(lowest_free(mask)[:, None], Hkv, axis=1)
+    prev[0] = -1 if i % 2 else prev[0]
+    ls = FillLockstep(wl, k, v, mask, prev, nsplit=nsplit)
+    for _ in range(int((mask == 0).sum(axis=1).max()) + 3):
+        ls.step()
+    assert ls.mask.all()
+    ls.finish()
 
 
 @pytest.mark.parametrize("case", _topk_cases(), ids=lambda c: f"t{c[0]}")
