@@ -194,6 +194,36 @@ def test_stack_projection_slice_lengths(H, Hq, Hkv):
     case.run(2)
 
 
+def _random_stack_cases():
+    rng = np.random.default_rng(20261205)
+    cases = []
+    while len(cases) < 8:
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.integers(1, 9))
+        Hq = G * Hkv
+        if (Hq * d) % 256:
+            continue
+        H = 256 * int(rng.integers(1, 10))
+        B = int(rng.integers(1, 41))
+        S = int(rng.integers(16, 401))
+        L = int(rng.integers(1, 3))
+        ns = int(rng.choice([0, 1, 2, 3]))
+        cases.append((len(cases), L, B, H, Hq, Hkv, d, S, ns or None))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_stack_cases(), ids=lambda c: f"s{c[0]}")
+def test_stack_random_shapes(case):
+    """Shapes drawn once from a fixed seed: hidden width, head counts, d,
+    batch, slots, depth and split count together (two steps each)."""
+    i, L, B, H, Hq, Hkv, d, S, nsplit = case
+    log(f"random stack {i}: L={L} B={B} H={H} Hq={Hq} Hkv={Hkv} d={d} S={S} nsplit={nsplit}")
+    case = StackCase(L=L, B=B, H=H, Hq=Hq, Hkv=Hkv, d=d, S=S, seed=12600 + i, kind="ragged",
+                     len_lo=max(1, S // 2), nsplit=nsplit, sample=sorted({0, B - 1}))
+    case.run(2)
+
+
 def test_stack_gqa8_d64():
     log("stack GQA 8, d 64")
     case = StackCase(L=2, B=4, H=512, Hq=16, Hkv=2, d=64, S=300, seed=12200, kind="sinks")
