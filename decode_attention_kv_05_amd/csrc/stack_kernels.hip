@@ -68,8 +68,9 @@ static_assert(kGemmSteps == kGemmWaves, "each wave stages one A fragment per row
 // Per stage j: the loads of A chunk j + 1 and of the weights of chunk j + 2
 // are issued first, then chunk j is multiplied, then A chunk j + 1 goes from
 // registers to LDS; one barrier per stage.  Loads complete in issue order,
-// so that last step waits for A alone and leaves the newest weights in
-// flight.  Every load is unconditional and the chunk loop is unrolled (NCH
+// so that last step waits for A chunk j + 1 and the loads before it (the
+// weights of chunk j + 1, needed next) and leaves the weights of chunk j + 2
+// in flight.  Every load is unconditional and the chunk loop is unrolled (NCH
 // chunks per slice), so the compiler counts outstanding loads exactly and
 // waits for no more than a step needs.
 template <int MT, int NCH>
