@@ -230,6 +230,17 @@ constexpr float kInf = __builtin_huge_valf();
 #ifndef LF_PV_DOT2
 #define LF_PV_DOT2 0
 #endif
+// Stagger of the streaming order in the split kernel: each wave starts at
+// batch (workgroup index * LF_ROTATE) mod (its batch count); 0 = in order.
+// Splits of a power-of-two number of rows otherwise stream in lockstep from
+// addresses a power of two apart (long_reasoning: 269.8 -> 248.6 us/step);
+// the single-split kernel measured no better staggered (ragged 3% slower).
+#ifndef LF_ROTATE
+#define LF_ROTATE 5
+#endif
+#ifndef LF_ROTATE_SINGLE
+#define LF_ROTATE_SINGLE 0  // also stagger the single-split kernel
+#endif
 // Issue the first V batch before the softmax-statistics barriers.
 #ifndef LF_PREFETCH_V
 #define LF_PREFETCH_V 0
@@ -407,7 +418,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   float mx[HPL];
 #pragma unroll
   for (int i = 0; i < HPL; ++i) mx[i] = kNegInf;
-  for (int r0 = wave * ROWS; r0 < n_eff; r0 += stride) {
+  // Batches of this wave, visited from a per-workgroup starting batch so
+  // that workgroups streaming at the same pace read addresses that differ
+  // by more than the power-of-two spacing of their cache rows.
+  const int nbatch = wave * ROWS < n_eff ? (n_eff - wave * ROWS + stride - 1) / stride : 0;
+  const int rot = LF_ROTATE && (SPLIT || LF_ROTATE_SINGLE) && nbatch > 0 ? (int)(((unsigned)item * LF_ROTATE) % (unsigned)nbatch) : 0;
+  for (int bi = 0; bi < nbatch; ++bi) {
+    const int r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
     uint4 buf[U];
     const uint32_t ok = load_batch<D, U, RPW>(buf, krs, mk, r0, rg, c);
     float* lrow = lg + (r0 + rg) * GP + hbase;
@@ -432,8 +449,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   // keeps going while the statistics are formed.
   uint4 vbuf[U];
   uint32_t vok = 0;
-  if (LF_PREFETCH_V && wave * ROWS < n_eff)
-    vok = load_batch<D, U, RPW>(vbuf, vrs, mk, wave * ROWS, rg, c);
+  if (LF_PREFETCH_V && nbatch > 0)
+    vok = load_batch<D, U, RPW>(vbuf, vrs, mk, wave * ROWS + rot * stride, rg, c);
 
   // ---- softmax statistics of this split
   // Lanes with equal c hold the same heads; fold the row groups, then waves.
@@ -519,8 +536,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
       *slot = sc;
     }
   };
-  for (int r0 = wave * ROWS; r0 < n_eff; r0 += stride) {
-    if (!LF_PREFETCH_V || r0 != wave * ROWS)
+  for (int bi = 0; bi < nbatch; ++bi) {
+    const int r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
+    if (!LF_PREFETCH_V || bi != 0)
       vok = load_batch<D, U, RPW>(vbuf, vrs, mk, r0, rg, c);
     float* lrow = lg + (r0 + rg) * GP;
     if constexpr (LF_PV_DOT2) {
