@@ -26,6 +26,13 @@ struct DecodeParams {
   uint64_t* cand;         // workspace: [pairs][chunks] packed (score, slot) minima
   uint32_t* ffree;        // workspace: [pairs][chunks] lowest free slot (fill step)
   uint8_t* mask_w;        // fill step: the same mask, updated in place; else null
+  uint64_t* xstat;        // team: [pairs][nsplit][GP][2] published (max, sum)
+  uint64_t* xfin;         // team: [pairs][nsplit][3] published minimum (high, low word), lowest free slot
+  uint64_t* xo;           // team: [pairs][nsplit][GP][d] published O accumulators
+  uint32_t* xcnt;         // team: [pairs] splits finished
+  size_t team_words;      // team: 32-bit words of the region above, zeroed before the launch
+  int pairs;              // B * Hkv
+  int pair0;              // team: first pair of this launch's round
   int Hq, Hkv, G, S, nsplit, split_len;
   int fill;               // 1: fill step (next slot = lowest free slot while any)
   float qscale;           // logit scale times log2(e)
@@ -38,8 +45,16 @@ struct TopkParams {
   int Hkv, S, k, pairs;
 };
 
+// team_grid > 0: after zeroing the team exchange words, cooperative launches
+// of at most team_grid workgroups (whole teams of prm.nsplit, one pair per
+// team) until every pair is done; otherwise nblocks
+// workgroups of the single-split kernel or of the split kernel followed by
+// the combine and finalize kernels.
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
-                         hipStream_t stream);
+                         int team_grid, hipStream_t stream);
+// Workgroups of the team kernel for (d, gp, nw, lds) that one compute unit
+// holds at once.
+hipError_t team_blocks_per_cu(int d, int gp, int nw, size_t lds, int* blocks);
 
 // One decode step after validation (the decode kernel and, for several
 // splits, the combine and finalize kernels).  mask_w non-null selects the
@@ -50,7 +65,7 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
                         void* k_cache, void* v_cache, const uint8_t* mask, uint8_t* mask_w,
                         const void* new_k, const void* new_v, const int32_t* prev_slot, void* out,
                         float* scores, int32_t* evict_slot, void* workspace, int nsplit,
-                        void* stream);
+                        int split_path, void* stream);
 hipError_t launch_topk(const TopkParams& prm, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 

@@ -66,8 +66,16 @@ struct WorkspaceLayout {
   size_t vnorm;     // float [pairs][S]: |v|_1 per slot
   size_t cand;      // uint64 [pairs][combine chunks]: per-chunk (score, slot) minima
   size_t ffree;     // uint32 [pairs][combine chunks]: per-chunk lowest free slot (fill step)
+  size_t team;      // team exchange region (see TeamLayout)
   size_t total;
 };
+
+// Exchange region of the team path.  Every word is a 64-bit (ready bit,
+// 32-bit payload) pair written once per step, so the region is zeroed before
+// each team launch; the counters come last.
+LF_HD inline size_t team_region_bytes(size_t pairs, int nsplit_eff, int gp, int d) {
+  return pairs * nsplit_eff * ((size_t)gp * 2 + 3 + (size_t)gp * d) * 8 + pairs * 4;
+}
 
 // Slots per workgroup of the split combine.
 constexpr int kCombineSlots = 2048;
@@ -91,11 +99,36 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
     off = align_up(off + pairs * (size_t)combine_chunks(S) * 8, 256);
     w.ffree = off;
     off = align_up(off + pairs * (size_t)combine_chunks(S) * 4, 256);
+    w.team = off;
+    off = align_up(off + team_region_bytes(pairs, nsplit_eff, gp, d), 256);
   } else {
-    w.part_ml = w.part_o = w.logit = w.vnorm = w.cand = w.ffree = off;
+    w.part_ml = w.part_o = w.logit = w.vnorm = w.cand = w.ffree = w.team = off;
   }
   w.total = off;
   return w;
+}
+
+// Words of the team region, in this order: published split (max, sum) per
+// head, published split results (minimum candidate high and low words, lowest
+// free slot), published split O accumulators, then the arrival counters.
+struct TeamLayout {
+  size_t xstat;   // uint64 [pairs][nsplit][GP][2]
+  size_t xfin;    // uint64 [pairs][nsplit][3]
+  size_t xo;      // uint64 [pairs][nsplit][GP][d]
+  size_t xcnt;    // uint32 [pairs]
+  size_t zero_words;  // uint32 words of the whole region
+};
+
+LF_HD inline TeamLayout team_layout(const WorkspaceLayout& w, int B, int Hkv, int d, int gp, int nsplit_eff) {
+  TeamLayout t{};
+  const size_t pairs = (size_t)B * (size_t)Hkv;
+  const size_t per = pairs * nsplit_eff;
+  t.xstat = w.team;
+  t.xfin = t.xstat + per * gp * 2 * 8;
+  t.xo = t.xfin + per * 3 * 8;
+  t.xcnt = t.xo + per * gp * (size_t)d * 8;
+  t.zero_words = team_region_bytes(pairs, nsplit_eff, gp, d) / 4;
+  return t;
 }
 
 // LDS layout of one workgroup, in bytes from the start of dynamic LDS.

@@ -192,12 +192,26 @@ int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void*
 
 namespace lf {
 
+// Workgroups of one team round for this step (whole teams, no more than
+// the device holds at once), or 0 when the device cannot hold a team.
+static int team_grid_for(int pairs, int d, int gp, int nw, size_t lds, int nsplit_eff) {
+  if (nsplit_eff < 2) return 0;
+  int per_cu = 0, cus = 0;
+  if (lf_device_num_cus(&cus) != LF_OK) return 0;
+  if (lf::team_blocks_per_cu(d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return 0;
+  const int64_t resident = (int64_t)per_cu * cus;
+  int64_t teams = resident / nsplit_eff;
+  if (teams > pairs) teams = pairs;
+  return (int)(teams * nsplit_eff);
+}
+
 // Enqueue one step after validation: the decode kernel, and for several
-// splits the combine and finalize kernels.
+// splits either one cooperative team launch or the combine and finalize
+// kernels.
 int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q, void* k_cache,
                  void* v_cache, const uint8_t* mask, uint8_t* mask_w, const void* new_k,
                  const void* new_v, const int32_t* prev_slot, void* out, float* scores,
-                 int32_t* evict_slot, void* workspace, int nsplit, void* stream) {
+                 int32_t* evict_slot, void* workspace, int nsplit, int split_path, void* stream) {
   const int G = Hq / Hkv;
   const int gp = lf::padded_group(G);
   int len, eff;
@@ -237,7 +251,19 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
   const int nblocks = B * Hkv * eff;
   const int nw = lf::decode_waves(gp, len);
   const size_t lds = lf::lds_layout(d, gp, len, nw).total;
-  return lf::launch_decode(prm, d, gp, nw, nblocks, lds, static_cast<hipStream_t>(stream)) ==
+  prm.pairs = B * Hkv;
+  int team_grid = 0;
+  if (eff > 1 && split_path != LF_SPLIT_COMBINE) {
+    const lf::TeamLayout tl = lf::team_layout(wl, B, Hkv, d, gp, eff);
+    team_grid = team_grid_for(B * Hkv, d, gp, nw, lds, eff);
+    if (team_grid == 0 && split_path == LF_SPLIT_TEAM) return LF_E_NSPLIT;
+    prm.xstat = reinterpret_cast<uint64_t*>(ws + tl.xstat);
+    prm.xfin = reinterpret_cast<uint64_t*>(ws + tl.xfin);
+    prm.xo = reinterpret_cast<uint64_t*>(ws + tl.xo);
+    prm.xcnt = reinterpret_cast<uint32_t*>(ws + tl.xcnt);
+    prm.team_words = tl.zero_words;
+  }
+  return lf::launch_decode(prm, d, gp, nw, nblocks, lds, team_grid, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? LF_OK
              : LF_E_HIP;
@@ -266,7 +292,7 @@ int longflow_decode_nsplit(int B, int Hq, int Hkv, int d, int S, float scale, co
   if (rc != LF_OK) return rc;
   if (B == 0) return LF_OK;
   return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, nullptr, new_k, new_v,
-                      prev_slot, out, scores, evict_slot, workspace, nsplit, stream);
+                      prev_slot, out, scores, evict_slot, workspace, nsplit, LF_SPLIT_AUTO, stream);
 }
 
 int longflow_decode(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
@@ -307,7 +333,31 @@ int longflow_decode_fill(int B, int Hq, int Hkv, int d, int S, float scale, cons
                      out, scores, next_slot, workspace, workspace_bytes, nsplit, true);
   if (rc != LF_OK) return rc;
   return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, mask, new_k, new_v,
-                      prev_slot, out, scores, next_slot, workspace, nsplit, stream);
+                      prev_slot, out, scores, next_slot, workspace, nsplit, LF_SPLIT_AUTO, stream);
+}
+
+int longflow_decode_ex(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                       void* k_cache, void* v_cache, uint8_t* mask, int fill, const void* new_k,
+                       const void* new_v, const int32_t* prev_slot, void* out, float* scores,
+                       int32_t* evict_slot, void* workspace, size_t workspace_bytes, int nsplit,
+                       int split_path, void* stream) {
+  int rc = lf_check_shape(B, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  if (nsplit < 0 || split_path < LF_SPLIT_AUTO || split_path > LF_SPLIT_TEAM) return LF_E_NSPLIT;
+  if (B == 0) return std::isfinite(scale) ? LF_OK : LF_E_VALUE;
+  if (nsplit == 0) {
+    int cus = 0;
+    rc = lf_device_num_cus(&cus);
+    if (rc != LF_OK) return rc;
+    rc = lf_plan_nsplit(B, Hq, Hkv, d, S, cus, &nsplit);
+    if (rc != LF_OK) return rc;
+  }
+  rc = validate_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v, prev_slot,
+                     out, scores, evict_slot, workspace, workspace_bytes, nsplit, fill != 0);
+  if (rc != LF_OK) return rc;
+  return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask,
+                                 fill ? mask : nullptr, new_k, new_v, prev_slot, out, scores,
+                                 evict_slot, workspace, nsplit, split_path, stream);
 }
 
 int longflow_evict_topk(int B, int Hkv, int S, int k, const float* scores, const uint8_t* mask,

@@ -277,8 +277,45 @@ __device__ __forceinline__ uint32_t load_batch(uint4 (&buf)[U], __amdgpu_buffer_
   return ok;
 }
 
-template <int D, int GP, int NW, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_kernel(DecodeParams p) {
+// How the workgroups of a launch share the pairs.
+constexpr int kModeSingle = 0;  // one workgroup per pair, the whole step on chip
+constexpr int kModeSplit = 1;   // one workgroup per split; combine kernels finish the step
+constexpr int kModeTeam = 2;    // a team of workgroups per pair (one per split), all
+                                // resident at once, exchanges softmax statistics mid-step
+
+// Polls a thread may spend on all of its team waits of one pair (at least
+// 128 clocks each: 3.5 ms or more in all) before it stops waiting and sets
+// LF_DEV_TEAM_TIMEOUT.  The members of a team run concurrently, so a wait
+// lasts about one split's phase K at most; it runs out only if a member is
+// kept from running (another process holding compute units), and then the
+// step still ends, flagged.
+constexpr int kTeamSpinLimit = 1 << 16;
+constexpr uint64_t kReady = 1ull << 32;
+
+// Publishes a float as a 64-bit word whose upper half marks it written.
+__device__ __forceinline__ void team_publish(uint64_t* w, float x) {
+  __hip_atomic_store(w, kReady | __float_as_uint(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits for a word published by another workgroup of the team, drawing on
+// the thread's poll budget; once the budget is gone it returns NaN at once.
+__device__ __forceinline__ float team_wait(const uint64_t* w, uint32_t* status, int& budget) {
+  for (;;) {
+    const uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v & kReady) return __uint_as_float((uint32_t)v);
+    if (budget <= 0) break;
+    --budget;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  atomicOr(status, LF_DEV_TEAM_TIMEOUT);
+  return __builtin_nanf("");
+}
+
+// One (pair, split) of a decode step.
+template <int D, int GP, int NW, int MODE>
+__device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int pair, int sp, int nsplit) {
+  constexpr bool SPLIT = MODE == kModeSplit;
+  constexpr bool TEAM = MODE == kModeTeam;
   using SH = Shape<D, GP>;
   constexpr int LPR = SH::LPR, RPW = SH::RPW, U = SH::U, ROWS = SH::ROWS;
   constexpr int HPL = SH::HPL, LPH = SH::LPH;
@@ -293,16 +330,6 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   const int c = lane % LPR;   // 16-byte column chunk of the row
   const int rg = lane / LPR;  // row within the wave load
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous run of work items so neighbouring splits share an L2.
-  const int nblk = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int per = nblk >> 3, rem = nblk & 7;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
-
-  const int nsplit = SPLIT ? p.nsplit : 1;
-  const int pair = item / nsplit;
-  const int sp = item - pair * nsplit;
   const int b = pair / p.Hkv;
   const int j = pair - b * p.Hkv;
   const int s0 = sp * p.split_len;
@@ -317,6 +344,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   uint64_t* best_w = reinterpret_cast<uint64_t*>(stat_il + GP);  // [NW]
   int* red_i = reinterpret_cast<int*>(best_w + NW);              // [NW]
   int* red_f = red_i + NW;                                       // [NW] fill step
+  int* last = red_f + NW;                                        // team: last to finish the pair
 
   const size_t row0 = (size_t)pair * p.S;  // first cache row of this pair
   const uint16_t* krows = p.k + (row0 + s0) * D;
@@ -422,7 +450,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   // that workgroups streaming at the same pace read addresses that differ
   // by more than the power-of-two spacing of their cache rows.
   const int nbatch = wave * ROWS < n_eff ? (n_eff - wave * ROWS + stride - 1) / stride : 0;
-  const int rot = LF_ROTATE && (SPLIT || LF_ROTATE_SINGLE) && nbatch > 0 ? (int)(((unsigned)item * LF_ROTATE) % (unsigned)nbatch) : 0;
+  const int rot = LF_ROTATE && (MODE != kModeSingle || LF_ROTATE_SINGLE) && nbatch > 0 ? (int)(((unsigned)item * LF_ROTATE) % (unsigned)nbatch) : 0;
   for (int bi = 0; bi < nbatch; ++bi) {
     const int r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
     uint4 buf[U];
@@ -481,11 +509,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     // Rows up to the end of the last batch (all written in phase K, -inf
     // when invalid) become e; invalid ones become exactly 0, so phase V
     // needs no per-row select.
+    // A team member keeps its logits until the pair's max is known: here it
+    // only sums exp2 against its own max.
     const int covered = (n_eff + ROWS - 1) / ROWS * ROWS;
     for (int r = tid / GP; r < covered; r += kThreads / GP) {
       const float s = lg[r * GP + h];
       const float e = (s == kNegInf) ? 0.f : exp2f(s - mh);
-      lg[r * GP + h] = e;
+      if (!TEAM) lg[r * GP + h] = e;
       lsum += e;
       if (SPLIT && r < n_eff) wl[r * GP + h] = s;
     }
@@ -498,6 +528,26 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
       float l = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) l += red[w * GP + tid];
+      if (TEAM) {
+        // Publish this split's (max, sum), then rebuild the pair's as the
+        // combine kernel does: max over the splits, then the rescaled sums
+        // in split order (a split without a finite logit adds its sum as it
+        // is: 0 when it has no valid slot, NaN when its logits are NaN).
+        uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2;
+        team_publish(xs + (sp * GP + tid) * 2, stat_m[tid]);
+        team_publish(xs + (sp * GP + tid) * 2 + 1, l);
+        int budget = kTeamSpinLimit;
+        float gm = kNegInf;
+        for (int q = 0; q < nsplit; ++q) gm = fmaxf(gm, team_wait(xs + (q * GP + tid) * 2, p.status, budget));
+        float gl = 0.f;
+        for (int q = 0; q < nsplit; ++q) {
+          const float mq = team_wait(xs + (q * GP + tid) * 2, p.status, budget);
+          const float lq = team_wait(xs + (q * GP + tid) * 2 + 1, p.status, budget);
+          gl += mq != kNegInf ? lq * exp2f(mq - gm) : lq;
+        }
+        stat_m[tid] = gm;
+        l = gl;
+      }
       stat_il[tid] = (l > 0.f || l != l) ? 1.0f / l : 0.f;  // NaN logits make every p NaN
       if (SPLIT) {
         float* ml = p.part_ml + (((size_t)pair * nsplit + sp) * GP + tid) * 2;
@@ -506,6 +556,16 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
       }
     }
     __syncthreads();
+    if (TEAM) {
+      // e against the pair's max, the same expression as with one split, so
+      // equal K/V rows get equal scores whichever split holds them.
+      const float gmh = stat_m[h];
+      for (int r = tid / GP; r < covered; r += kThreads / GP) {
+        const float s = lg[r * GP + h];
+        lg[r * GP + h] = (s == kNegInf) ? 0.f : exp2f(s - gmh);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- phase V: O accumulators, |v|_1, and (single split) scores
@@ -628,7 +688,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   }
   __syncthreads();
 
-  if (!SPLIT) {
+  if (MODE == kModeSingle) {
     for (int idx = tid; idx < GP * D; idx += kThreads) {
       const int h = idx / D;
       if (h >= p.G) continue;
@@ -652,7 +712,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
       }
       p.evict[pair] = next;
     }
-  } else {
+  } else if (SPLIT) {
+    // The split's O accumulators, against the split's own max.
     float* po = p.part_o + ((size_t)pair * nsplit + sp) * GP * D;
     for (int idx = tid; idx < GP * D; idx += kThreads) {
       float o = 0.f;
@@ -660,6 +721,81 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
       for (int w = 0; w < NW; ++w) o += ored[w * GP * D + idx];
       po[idx] = o;
     }
+  }
+  if (TEAM) {
+    // Publish this split's O accumulators and results, count it in; the
+    // team's last split to arrive waits for the others' words, sums them in
+    // split order and writes O and the slot.  Every word carries its own
+    // ready bit, so no fence orders them against the count.
+    uint64_t* xo = p.xo + ((size_t)pair * nsplit + sp) * GP * D;
+    for (int idx = tid; idx < GP * D; idx += kThreads) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) o += ored[w * GP * D + idx];
+      team_publish(xo + idx, o);
+    }
+    if (tid == 0) {
+      uint64_t m = best_w[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) m = best_w[w] < m ? best_w[w] : m;
+      int ff = INT_MAX;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ff = min(ff, red_f[w]);
+      uint64_t* xf = p.xfin + ((size_t)pair * nsplit + sp) * 3;
+      team_publish(xf, __uint_as_float((uint32_t)(m >> 32)));
+      team_publish(xf + 1, __uint_as_float((uint32_t)m));
+      team_publish(xf + 2, __uint_as_float(p.fill && ff != INT_MAX ? (uint32_t)(s0 + ff) : (uint32_t)INT_MAX));
+    }
+    __syncthreads();
+    if (tid == 0) *last = atomicAdd(p.xcnt + pair, 1u) == (unsigned)(nsplit - 1);
+    __syncthreads();
+    if (*last) {
+      int budget = kTeamSpinLimit;
+      const uint64_t* xa = p.xo + (size_t)pair * nsplit * GP * D;
+      for (int idx = tid; idx < GP * D; idx += kThreads) {
+        const int h = idx / D;
+        if (h >= p.G) continue;
+        float o = 0.f;
+        for (int q = 0; q < nsplit; ++q) o += team_wait(xa + (size_t)q * GP * D + idx, p.status, budget);
+        p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] = f32_to_bf16_rne(o * stat_il[h]);
+      }
+      if (tid == 0) {
+        uint64_t m = kNoCandidate;
+        uint32_t ff = (uint32_t)INT_MAX;
+        for (int q = 0; q < nsplit; ++q) {
+          const uint64_t* xf = p.xfin + ((size_t)pair * nsplit + q) * 3;
+          const uint64_t hi = __float_as_uint(team_wait(xf, p.status, budget));
+          const uint64_t lo = __float_as_uint(team_wait(xf + 1, p.status, budget));
+          const uint64_t cq = hi << 32 | lo;
+          m = cq < m ? cq : m;
+          ff = min(ff, __float_as_uint(team_wait(xf + 2, p.status, budget)));
+        }
+        int32_t next = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
+        if (p.fill && ff != (uint32_t)INT_MAX) next = (int32_t)ff;
+        p.evict[pair] = next;
+      }
+    }
+  }
+}
+
+template <int D, int GP, int NW, int MODE>
+__global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_kernel(DecodeParams p) {
+  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+  // contiguous run of work items so neighbouring splits share an L2.
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
+  const int nsplit = MODE == kModeSingle ? 1 : p.nsplit;
+  const int first = item / nsplit;
+  const int sp = item - first * nsplit;
+  if constexpr (MODE == kModeTeam) {
+    // One round of whole teams, no more than the device holds at once: team
+    // t takes pair pair0 + t.  (A persistent loop over the pairs would keep
+    // the parameters live across it and spill.)
+    decode_pair<D, GP, NW, MODE>(p, item, p.pair0 + first, sp, nsplit);
+  } else {
+    decode_pair<D, GP, NW, MODE>(p, item, first, sp, nsplit);
   }
 }
 
@@ -866,9 +1002,28 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
 // ------------------------------------------------------------------ launch
 
 template <int D, int GP, int NW>
-hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, hipStream_t stream) {
+hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, int team_grid, hipStream_t stream) {
+  if (team_grid > 0) {
+    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(prm.xstat), prm.team_words, 0u, stream);
+    if (e != hipSuccess) return e;
+    // Rounds of at most team_grid / nsplit teams, one pair each; team_grid
+    // is what the device holds at once, so an idle device runs a round's
+    // workgroups together.  (A cooperative launch would promise it, but
+    // costs 11-19 us more per launch than a plain one.)
+    const int teams = team_grid / prm.nsplit;
+    for (int p0 = 0; p0 < prm.pairs; p0 += teams) {
+      DecodeParams arg = prm;
+      arg.pair0 = p0;
+      const int nt = prm.pairs - p0 < teams ? prm.pairs - p0 : teams;
+      hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeTeam>), dim3(nt * prm.nsplit), dim3(NW * 64),
+                         lds, stream, arg);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (prm.nsplit > 1) {
-    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, true>), dim3(nblocks), dim3(NW * 64), lds,
+    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeSplit>), dim3(nblocks), dim3(NW * 64), lds,
                        stream, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -881,35 +1036,68 @@ hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, hipStrea
     hipLaunchKernelGGL(longflow_finalize_kernel, dim3((pairs + 255) / 256), dim3(256), 0, stream,
                        prm, pairs, nchunk);
   } else {
-    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, false>), dim3(nblocks), dim3(NW * 64), lds,
+    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeSingle>), dim3(nblocks), dim3(NW * 64), lds,
                        stream, prm);
   }
   return hipGetLastError();
 }
 
 template <int D, int GP>
-hipError_t launch_dg(const DecodeParams& prm, int nw, int nblocks, size_t lds, hipStream_t stream) {
-  if (nw == LF_WAVES_LARGE_LDS) return launch_dgw<D, GP, LF_WAVES_LARGE_LDS>(prm, nblocks, lds, stream);
-  if (nw == LF_WAVES_SMALL_LDS) return launch_dgw<D, GP, LF_WAVES_SMALL_LDS>(prm, nblocks, lds, stream);
+hipError_t launch_dg(const DecodeParams& prm, int nw, int nblocks, size_t lds, int team_grid, hipStream_t stream) {
+  if (nw == LF_WAVES_LARGE_LDS) return launch_dgw<D, GP, LF_WAVES_LARGE_LDS>(prm, nblocks, lds, team_grid, stream);
+  if (nw == LF_WAVES_SMALL_LDS) return launch_dgw<D, GP, LF_WAVES_SMALL_LDS>(prm, nblocks, lds, team_grid, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D, int GP>
+hipError_t team_occupancy_dg(int nw, size_t lds, int* blocks) {
+  if (nw == LF_WAVES_LARGE_LDS)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, LF_WAVES_LARGE_LDS, kModeTeam>),
+        LF_WAVES_LARGE_LDS * 64, lds);
+  if (nw == LF_WAVES_SMALL_LDS)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, LF_WAVES_SMALL_LDS, kModeTeam>),
+        LF_WAVES_SMALL_LDS * 64, lds);
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams& prm, int gp, int nw, int nblocks, size_t lds, hipStream_t stream) {
+hipError_t team_occupancy_d(int gp, int nw, size_t lds, int* blocks) {
   switch (gp) {
-    case 1: return launch_dg<D, 1>(prm, nw, nblocks, lds, stream);
-    case 2: return launch_dg<D, 2>(prm, nw, nblocks, lds, stream);
-    case 4: return launch_dg<D, 4>(prm, nw, nblocks, lds, stream);
-    case 8: return launch_dg<D, 8>(prm, nw, nblocks, lds, stream);
+    case 1: return team_occupancy_dg<D, 1>(nw, lds, blocks);
+    case 2: return team_occupancy_dg<D, 2>(nw, lds, blocks);
+    case 4: return team_occupancy_dg<D, 4>(nw, lds, blocks);
+    case 8: return team_occupancy_dg<D, 8>(nw, lds, blocks);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t team_blocks_per_cu(int d, int gp, int nw, size_t lds, int* blocks) {
+  switch (d) {
+    case 64: return team_occupancy_d<64>(gp, nw, lds, blocks);
+    case 128: return team_occupancy_d<128>(gp, nw, lds, blocks);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& prm, int gp, int nw, int nblocks, size_t lds, int team_grid,
+                    hipStream_t stream) {
+  switch (gp) {
+    case 1: return launch_dg<D, 1>(prm, nw, nblocks, lds, team_grid, stream);
+    case 2: return launch_dg<D, 2>(prm, nw, nblocks, lds, team_grid, stream);
+    case 4: return launch_dg<D, 4>(prm, nw, nblocks, lds, team_grid, stream);
+    case 8: return launch_dg<D, 8>(prm, nw, nblocks, lds, team_grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
-                         hipStream_t stream) {
+                         int team_grid, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_d<64>(prm, gp, nw, nblocks, lds, stream);
-    case 128: return launch_d<128>(prm, gp, nw, nblocks, lds, stream);
+    case 64: return launch_d<64>(prm, gp, nw, nblocks, lds, team_grid, stream);
+    case 128: return launch_d<128>(prm, gp, nw, nblocks, lds, team_grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

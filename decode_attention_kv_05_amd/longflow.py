@@ -26,11 +26,16 @@ LF_E_VALUE = -8
 LF_DEV_BAD_PREV = 0x1
 LF_DEV_WRITE_MASKED = 0x2
 LF_DEV_FILL_DIVERGED = 0x4
+LF_DEV_TEAM_TIMEOUT = 0x8
+
+LF_SPLIT_AUTO, LF_SPLIT_COMBINE, LF_SPLIT_TEAM = 0, 1, 2
+SPLIT_PATHS = {"auto": LF_SPLIT_AUTO, "combine": LF_SPLIT_COMBINE, "team": LF_SPLIT_TEAM}
 
 EXPORTED = (
     "lf_version", "lf_strerror", "lf_check_shape", "lf_plan_nsplit", "lf_workspace_size",
     "lf_device_num_cus", "lf_workspace_init", "lf_validate", "longflow_decode",
-    "longflow_decode_nsplit", "longflow_decode_fill", "longflow_evict_topk", "lf_read_device_status",
+    "longflow_decode_nsplit", "longflow_decode_fill", "longflow_decode_ex", "longflow_evict_topk",
+    "lf_read_device_status",
     "lf_stack_workspace_size", "longflow_stack_step", "lf_stack_graph_create", "lf_graph_launch",
     "lf_graph_destroy",
 )
@@ -54,6 +59,7 @@ def _load():
         "longflow_decode": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _p], _i),
         "longflow_decode_nsplit": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i, _p], _i),
         "longflow_decode_fill": ([_i] * 5 + [_f] + [_p] * 11 + [_sz, _i, _p], _i),
+        "longflow_decode_ex": ([_i] * 5 + [_f] + [_p] * 4 + [_i] + [_p] * 7 + [_sz, _i, _i, _p], _i),
         "longflow_evict_topk": ([_i] * 4 + [_p] * 3 + [_p], _i),
         "lf_read_device_status": ([_p, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
         "lf_stack_workspace_size": ([_i] * 8 + [ctypes.POINTER(_sz)], _i),
@@ -161,7 +167,7 @@ def _need(t, name, dtype, shape, device):
 
 
 def _step(entry, q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out, scores, evict_slot,
-          workspace, nsplit, stream):
+          workspace, nsplit, stream, split_path=None):
     B, Hq, d = q.shape
     Hkv, S = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
@@ -190,18 +196,28 @@ def _step(entry, q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the device of q")
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
-    rc = getattr(_lib, entry)(
-        B, Hq, Hkv, d, S, float(scale), ptr(q), ptr(k_cache), ptr(v_cache), ptr(mask),
-        ptr(new_k), ptr(new_v), ptr(prev_slot), ptr(out), ptr(scores), ptr(evict_slot),
-        ptr(workspace), workspace.numel() * workspace.element_size(), int(nsplit),
-        _stream_ptr(stream, dev))
+    if split_path is None:
+        rc = getattr(_lib, entry)(
+            B, Hq, Hkv, d, S, float(scale), ptr(q), ptr(k_cache), ptr(v_cache), ptr(mask),
+            ptr(new_k), ptr(new_v), ptr(prev_slot), ptr(out), ptr(scores), ptr(evict_slot),
+            ptr(workspace), workspace.numel() * workspace.element_size(), int(nsplit),
+            _stream_ptr(stream, dev))
+    else:
+        if split_path not in SPLIT_PATHS:
+            raise ValueError(f"split_path must be one of {sorted(SPLIT_PATHS)}, got {split_path!r}")
+        fill = 1 if entry == "longflow_decode_fill" else 0
+        entry = "longflow_decode_ex"
+        rc = _lib.longflow_decode_ex(
+            B, Hq, Hkv, d, S, float(scale), ptr(q), ptr(k_cache), ptr(v_cache), ptr(mask), fill, ptr(new_k), ptr(new_v), ptr(prev_slot), ptr(out), ptr(scores),
+            ptr(evict_slot), ptr(workspace), workspace.numel() * workspace.element_size(), int(nsplit),
+            SPLIT_PATHS[split_path], _stream_ptr(stream, dev))
     _check(rc, entry)
     return out, scores, evict_slot
 
 
 def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
                     out=None, scores=None, evict_slot=None, workspace=None, nsplit=None,
-                    stream=None):
+                    stream=None, split_path=None):
     """One fused decode step; returns (out, scores, evict_slot).
 
     q [B, Hq, d] bf16; k_cache, v_cache [B, Hkv, S, d] bf16 (updated in place);
@@ -210,15 +226,17 @@ def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale
     bf16, scores [B, Hkv, S] float32, evict_slot [B, Hkv] int32.  scale
     defaults to 1/sqrt(d).  nsplit None uses the library's plan for the
     device.  The work is enqueued on `stream` (default: torch's current
-    stream) and not waited for.
+    stream) and not waited for.  split_path ("auto", "combine", "team"; None
+    = "auto") chooses how a step with several splits is finished
+    (longflow_decode_ex).
     """
     return _step("longflow_decode_nsplit", q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
-                 scores, evict_slot, workspace, nsplit, stream)
+                 scores, evict_slot, workspace, nsplit, stream, split_path)
 
 
 def longflow_decode_fill(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
                          out=None, scores=None, next_slot=None, workspace=None, nsplit=None,
-                         stream=None):
+                         stream=None, split_path=None):
     """One decode step of the fill phase; returns (out, scores, next_slot).
 
     As longflow_decode, except that `mask` is updated in place (the written
@@ -226,7 +244,7 @@ def longflow_decode_fill(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, 
     mask while the sequence has one, else the evicted slot.
     """
     return _step("longflow_decode_fill", q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
-                 scores, next_slot, workspace, nsplit, stream)
+                 scores, next_slot, workspace, nsplit, stream, split_path)
 
 
 def longflow_evict_topk(scores, mask, k, *, out=None, stream=None):

@@ -92,6 +92,25 @@ typedef enum lf_status {
 #define LF_DEV_WRITE_MASKED 0x2u /* prev_slot named a masked slot: written, unused */
 #define LF_DEV_FILL_DIVERGED 0x4u /* fill step: the KV heads of a sequence did not all
                                      write the same free slot (see longflow_decode_fill) */
+#define LF_DEV_TEAM_TIMEOUT 0x8u  /* team path: a split waited too long for the
+                                     other splits of its pair, which happens only
+                                     when they were kept from running at the same
+                                     time (another process holding compute units);
+                                     that step's results are unspecified */
+
+/* How a step with several slot splits per (b, j) pair is finished. */
+#define LF_SPLIT_AUTO 0    /* LF_SPLIT_TEAM when the device can hold a team, else
+                              LF_SPLIT_COMBINE */
+#define LF_SPLIT_COMBINE 1 /* each split writes its logits, |v|_1 and partial
+                              softmax statistics to the workspace; a combine and
+                              a finalize kernel rescale them to the true softmax */
+#define LF_SPLIT_TEAM 2    /* the splits of a pair run together as a team of
+                              workgroups, exchange their (max, sum) through the
+                              workspace mid-step, and score their slots against
+                              the pair's softmax with the logits kept on chip;
+                              the last split of a pair to finish writes O and
+                              the evicted slot.  Launched in rounds of whole
+                              teams no larger than the device holds at once */
 
 /* ABI version (LF_ABI_VERSION). */
 int lf_version(void);
@@ -173,6 +192,30 @@ int longflow_decode_fill(int B, int Hq, int Hkv, int d, int S, float scale,
                          const void* new_k, const void* new_v, const int32_t* prev_slot,
                          void* out, float* scores, int32_t* next_slot, void* workspace,
                          size_t workspace_bytes, int nsplit, void* stream);
+
+/* The general form of longflow_decode_nsplit and longflow_decode_fill:
+ *   fill        0: mask is read only (longflow_decode_nsplit);
+ *               1: fill step, mask updated in place (longflow_decode_fill)
+ *   nsplit      0 = the count lf_plan_nsplit chooses for the current device
+ *   split_path  LF_SPLIT_AUTO, LF_SPLIT_COMBINE or LF_SPLIT_TEAM: how a step
+ *               with nsplit > 1 is finished (ignored when nsplit = 1).
+ *               LF_SPLIT_TEAM returns LF_E_NSPLIT when the device cannot hold
+ *               a whole team of nsplit workgroups at once.
+ * Both paths compute the same operator (Figure 2: the split is the
+ * flash-decoding form of one attention pass; abstract: attention, scoring and
+ * eviction fused in one operator).  The team path reads K and V once and
+ * keeps the logits on chip; the scores are those of the combine path, O may
+ * differ by rounding.  The team path needs every workgroup of a round
+ * running at once, which an otherwise idle device provides; where another
+ * process shares the compute units, use LF_SPLIT_COMBINE (the team path
+ * then may set LF_DEV_TEAM_TIMEOUT).  Same workspace size as
+ * longflow_decode_nsplit. */
+int longflow_decode_ex(int B, int Hq, int Hkv, int d, int S, float scale,
+                       const void* q, void* k_cache, void* v_cache, uint8_t* mask,
+                       int fill, const void* new_k, const void* new_v,
+                       const int32_t* prev_slot, void* out, float* scores,
+                       int32_t* evict_slot, void* workspace, size_t workspace_bytes,
+                       int nsplit, int split_path, void* stream);
 
 /* Several slots evicted at once, for a periodic cadence (compress every N
  * steps instead of every step).  For every (b, j): the set of the k valid

@@ -18,6 +18,18 @@ SCORE_RTOL = 1e-3
 TIE_RTOL = 1e-4
 
 
+def split_variants(counts):
+    """(nsplit, split_path) cases: one per count of 1 (or None, the plan),
+    both finishing paths for every count above 1."""
+    out = []
+    for n in counts:
+        if n is None or n == 1:
+            out.append((n, None))
+        else:
+            out += [(n, "team"), (n, "combine")]
+    return out
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -69,11 +81,12 @@ class Lockstep:
     in `pairs` (None = all), on the oracle; both sides continue from the GPU's
     accepted eviction."""
 
-    def __init__(self, wl, pairs=None, nsplit=None, device="cuda", state=None):
+    def __init__(self, wl, pairs=None, nsplit=None, device="cuda", state=None, split_path=None):
         from decode_attention_kv_05_amd import longflow as lf
         self.lf = lf
         self.wl = wl
         self.nsplit = nsplit
+        self.split_path = split_path
         self.device = device
         if state is None:
             k, v, mask = W.initial_cache(wl)
@@ -99,7 +112,7 @@ class Lockstep:
         out, sc, ev = self.lf.longflow_decode(
             bf16_dev(q, self.device), self.dk, self.dv, self.dm, bf16_dev(nk, self.device),
             bf16_dev(nv, self.device), self.dprev, scale=float(self.wl.scale), workspace=self.ws,
-            nsplit=self.nsplit)
+            nsplit=self.nsplit, split_path=self.split_path)
         torch.cuda.synchronize()
         return (q, nk, nv), out, sc, ev
 
@@ -186,9 +199,9 @@ class FillLockstep:
     """Fill steps on the GPU and in the oracle from the same state; both sides
     continue from the GPU's next slot once it has been accepted."""
 
-    def __init__(self, wl, k, v, mask, prev, nsplit=None):
+    def __init__(self, wl, k, v, mask, prev, nsplit=None, split_path=None):
         from decode_attention_kv_05_amd import longflow as lf
-        self.lf, self.wl, self.nsplit = lf, wl, nsplit
+        self.lf, self.wl, self.nsplit, self.split_path = lf, wl, nsplit, split_path
         self.k_ref, self.v_ref, self.mask = k, v, mask.copy()
         self.dk, self.dv = bf16_dev(k), bf16_dev(v)
         self.dm = torch.from_numpy(mask.copy()).cuda()
@@ -204,7 +217,8 @@ class FillLockstep:
         q, nk, nv = W.step_inputs(wl, t)
         entry = self.lf.longflow_decode_fill if use_fill else self.lf.longflow_decode
         out, sc, nx = entry(bf16_dev(q), self.dk, self.dv, self.dm, bf16_dev(nk), bf16_dev(nv), self.dprev,
-                            scale=float(wl.scale), workspace=self.ws, nsplit=self.nsplit)
+                            scale=float(wl.scale), workspace=self.ws, nsplit=self.nsplit,
+                            split_path=self.split_path)
         torch.cuda.synchronize()
         if use_fill:
             o_ref, s_ref, n_ref, m_ref = decode_step_fill(q, self.k_ref, self.v_ref, self.mask, nk, nv,

@@ -193,8 +193,37 @@ def test_fill_mask_is_written(a, b):
     assert f.call(**{a: f.addr[b]}) == lf.LF_OK
 
 
+def _ex_call(f, fill=0, nsplit=1, split_path=0, shape=None, **over):
+    """longflow_decode_ex on fake addresses (argument errors only)."""
+    a = dict(f.addr, **over)
+    P = lambda x: ctypes.c_void_p(x)
+    return lf._lib.longflow_decode_ex(
+        *(shape or f.shape), 0.1, P(a["q"]), P(a["k"]), P(a["v"]), P(a["mask"]), fill, P(a["nk"]), P(a["nv"]),
+        P(a["prev"]), P(a["out"]), P(a["scores"]), P(a["evict"]), P(a["ws"]), f.ws_bytes, nsplit, split_path, None)
+
+
+def test_general_entry_argument_errors():
+    """longflow_decode_ex: the split path must be one of the three, the split
+    count non-negative; with fill = 1 the mask is written (so it may not share
+    memory with an input), with fill = 0 it is only read."""
+    f = Fake()
+    assert (lf.LF_SPLIT_AUTO, lf.LF_SPLIT_COMBINE, lf.LF_SPLIT_TEAM) == (0, 1, 2)
+    assert _ex_call(f, split_path=3) == lf.LF_E_NSPLIT
+    assert _ex_call(f, split_path=-1) == lf.LF_E_NSPLIT
+    assert _ex_call(f, nsplit=-1) == lf.LF_E_NSPLIT
+    assert _ex_call(f, nsplit=101) == lf.LF_E_NSPLIT
+    assert _ex_call(f, q=0) == lf.LF_E_NULL
+    assert _ex_call(f, fill=1, mask=f.addr["q"]) == lf.LF_E_ALIAS
+    assert _ex_call(f, shape=(2, 8, 3, 128, 100)) == lf.LF_E_SHAPE
+    zeros = {n: 0 for n in f.addr}
+    assert _ex_call(f, shape=(0, 8, 2, 128, 100), split_path=2, **zeros) == lf.LF_OK
+
+
 def test_fill_workspace_has_free_slot_minima():
-    """Split workspaces hold one 32-bit lowest-free-slot word per combine chunk."""
+    """Split workspaces hold one 32-bit lowest-free-slot word per combine chunk,
+    then the team path's exchange region: per split of a pair 64-bit words for
+    its (max, sum) per padded head, its three results and its O accumulators,
+    and one 32-bit counter per pair."""
     B, Hq, Hkv, d, S = 4, 16, 2, 128, 5000
     one = lf.lf_workspace_size(B, Hq, Hkv, d, S, 1)
     assert one == 256
@@ -204,7 +233,7 @@ def test_fill_workspace_has_free_slot_minima():
     split = 3
     expect = 256
     for n in (pairs * split * gp * 2 * 4, pairs * split * gp * d * 4, pairs * S * gp * 4, pairs * S * 4,
-              pairs * chunks * 8, pairs * chunks * 4):
+              pairs * chunks * 8, pairs * chunks * 4, pairs * split * (gp * 2 + 3 + gp * d) * 8 + pairs * 4):
         expect += -(-n // 256) * 256
     assert lf.lf_workspace_size(B, Hq, Hkv, d, S, split) == expect
 

@@ -46,3 +46,17 @@ def test_full_workload(name):
                 log(f"  step {t} ok")
     ls.check_full_cache()
     log(f"  evictions exactly equal to the oracle's: {ls.exact}/{ls.total}")
+
+
+def test_full_long_reasoning_combine_path():
+    """The long-reasoning cache at full size through the other way of
+    finishing its split steps (logits through the workspace, combine and
+    finalize kernels), for 8 steps."""
+    wl = W.WORKLOADS["long_reasoning"].replace(steps=8)
+    pairs = sample_pairs(wl)
+    log(f"long_reasoning, combine path, {wl.steps} steps, pairs={pairs}")
+    ls = Lockstep(wl, pairs=pairs, nsplit=4, split_path="combine")
+    for t in range(wl.steps):
+        out, sc, ev = ls.step()
+        global_properties(sc, ev, ls.dm)
+    ls.check_full_cache()

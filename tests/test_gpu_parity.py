@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from decode_attention_kv_05_amd import workloads as W
-from gpu_util import Lockstep, bf16_dev, bf16_host, bf16_value, global_properties, log
+from gpu_util import Lockstep, bf16_dev, bf16_host, bf16_value, global_properties, log, split_variants
 
 pytestmark = pytest.mark.gpu
 
@@ -25,22 +25,22 @@ def _device():
     yield
 
 
-@pytest.mark.parametrize("nsplit", [None, 1, 2, 3, 7])
-def test_tiny_workload_lockstep(nsplit):
+@pytest.mark.parametrize("nsplit,path", split_variants([None, 1, 2, 3, 7]))
+def test_tiny_workload_lockstep(nsplit, path):
     wl = W.WORKLOADS["tiny"]
-    log(f"tiny lockstep nsplit={nsplit}")
-    ls = Lockstep(wl, nsplit=nsplit)
+    log(f"tiny lockstep nsplit={nsplit} path={path}")
+    ls = Lockstep(wl, nsplit=nsplit, split_path=path)
     for _ in range(wl.steps):
         ls.step()
     ls.check_full_cache()
 
 
-@pytest.mark.parametrize("nsplit", [1, 4])
-def test_tiny_d128(nsplit):
+@pytest.mark.parametrize("nsplit,path", split_variants([1, 4]))
+def test_tiny_d128(nsplit, path):
     """d = 128 makes the scale 1/sqrt(128), not a power of two."""
     wl = W.WORKLOADS["tiny"].replace(name="tiny_d128", d=128)
-    log(f"tiny d128 nsplit={nsplit}")
-    ls = Lockstep(wl, nsplit=nsplit)
+    log(f"tiny d128 nsplit={nsplit} path={path}")
+    ls = Lockstep(wl, nsplit=nsplit, split_path=path)
     for _ in range(wl.steps):
         ls.step()
     ls.check_full_cache()
@@ -48,14 +48,14 @@ def test_tiny_d128(nsplit):
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("nsplit", [1, 3])
-def test_group_sizes_ragged_tail(G, d, nsplit):
+@pytest.mark.parametrize("nsplit,path", split_variants([1, 3]))
+def test_group_sizes_ragged_tail(G, d, nsplit, path):
     """GQA groups 1..8 (3 and 5 padded to 4 and 8), a slot count that is not
     a multiple of any tile, and ragged per-sequence valid lengths."""
     wl = W.Workload(f"g{G}_d{d}", B=3, Hq=2 * G, Hkv=2, d=d, S=333, steps=4, kind="ragged",
                     seed=7000 + G, len_lo=40)
-    log(f"group G={G} d={d} nsplit={nsplit}")
-    ls = Lockstep(wl, nsplit=nsplit)
+    log(f"group G={G} d={d} nsplit={nsplit} path={path}")
+    ls = Lockstep(wl, nsplit=nsplit, split_path=path)
     for _ in range(wl.steps):
         ls.step()
     ls.check_full_cache()
@@ -86,12 +86,12 @@ def _empty_row_case(nsplit):
     return wl, (k, v, mask)
 
 
-@pytest.mark.parametrize("nsplit", [1, 3])
-def test_empty_and_single_slot_rows(nsplit):
+@pytest.mark.parametrize("nsplit,path", split_variants([1, 3]))
+def test_empty_and_single_slot_rows(nsplit, path):
     wl, state = _empty_row_case(nsplit)
     k, v, mask = state
-    log(f"empty/single rows nsplit={nsplit}")
-    ls = Lockstep(wl, nsplit=nsplit, state=(k.copy(), v.copy(), mask.copy()))
+    log(f"empty/single rows nsplit={nsplit} path={path}")
+    ls = Lockstep(wl, nsplit=nsplit, state=(k.copy(), v.copy(), mask.copy()), split_path=path)
     out, sc, ev = ls.step()
     ev = ev.cpu().numpy()
     assert np.all(ev[1] == -1) and np.all(ev[2] == 57)
@@ -103,26 +103,26 @@ def test_empty_and_single_slot_rows(nsplit):
         assert np.array_equal(o[2, 2 * j], vv) and np.array_equal(o[2, 2 * j + 1], vv)
 
 
-@pytest.mark.parametrize("nsplit", [1, 4])
-def test_prev_slot_status_flags(nsplit):
+@pytest.mark.parametrize("nsplit,path", split_variants([1, 4]))
+def test_prev_slot_status_flags(nsplit, path):
     from decode_attention_kv_05_amd import longflow as lf
     wl = W.Workload("flags", B=2, Hq=8, Hkv=2, d=64, S=64, steps=1, seed=43, valid=48)
     k, v, mask = W.initial_cache(wl)
     q, nk, nv = W.step_inputs(wl, 0)
     dk, dv = bf16_dev(k), bf16_dev(v)
     ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, nsplit)
-    log(f"status flags nsplit={nsplit}")
+    log(f"status flags nsplit={nsplit} path={path}")
     # out of range: no write anywhere, flag set
     prev = torch.tensor([[64, -5], [-1, -1]], dtype=torch.int32, device="cuda")
     lf.longflow_decode(bf16_dev(q), dk, dv, torch.from_numpy(mask).cuda(), bf16_dev(nk), bf16_dev(nv), prev,
-                       workspace=ws, nsplit=nsplit)
+                       workspace=ws, nsplit=nsplit, split_path=path)
     assert lf.lf_read_device_status(ws) == lf.LF_DEV_BAD_PREV
     assert np.array_equal(bf16_host(dk), k) and np.array_equal(bf16_host(dv), v)
     # masked target: written, flagged, and invisible to the result
     lf.lf_workspace_init(ws)
     prev = torch.tensor([[50, -1], [-1, 3]], dtype=torch.int32, device="cuda")
     out, sc, ev = lf.longflow_decode(bf16_dev(q), dk, dv, torch.from_numpy(mask).cuda(), bf16_dev(nk),
-                                     bf16_dev(nv), prev, workspace=ws, nsplit=nsplit)
+                                     bf16_dev(nv), prev, workspace=ws, nsplit=nsplit, split_path=path)
     assert lf.lf_read_device_status(ws) == lf.LF_DEV_WRITE_MASKED
     assert np.array_equal(bf16_host(dk[0, 0, 50]), nk[0, 0])
     assert np.array_equal(bf16_host(dk[1, 1, 3]), nk[1, 1])
@@ -143,14 +143,16 @@ def test_nan_in_valid_slots_same_for_every_split_count():
     q, nk, nv = W.step_inputs(wl, 0)
     prev = torch.full((wl.B, wl.Hkv), -1, dtype=torch.int32, device="cuda")
     res = []
-    for nsplit in (1, 4):
-        log(f"NaN keys, nsplit={nsplit}")
+    for nsplit, path in split_variants((1, 4)):
+        log(f"NaN keys, nsplit={nsplit} path={path}")
         out, sc, ev = lf.longflow_decode(bf16_dev(q), bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda(),
-                                         bf16_dev(nk), bf16_dev(nv), prev, nsplit=nsplit)
+                                         bf16_dev(nk), bf16_dev(nv), prev, nsplit=nsplit, split_path=path)
         torch.cuda.synchronize()
         res.append((bf16_value(bf16_host(out)), sc.cpu().numpy()))
-    (o1, s1), (o4, s4) = res
-    assert np.array_equal(np.isnan(o1), np.isnan(o4)) and np.array_equal(np.isnan(s1), np.isnan(s4))
+    (o1, s1), *rest = res
+    for o4, s4 in rest:
+        assert np.array_equal(np.isnan(o1), np.isnan(o4)) and np.array_equal(np.isnan(s1), np.isnan(s4))
+    o4 = rest[0][0]
     assert np.isnan(o1[0, 0:2]).all() and np.isnan(o1[1, 2:4]).all()
     assert not np.isnan(o1[0, 2:4]).any() and not np.isnan(o1[1, 0:2]).any()
     assert np.isnan(s1[0, 0]).all() and not np.isnan(s1[0, 1]).any()
@@ -167,8 +169,8 @@ def test_empty_batch_is_a_no_op():
     assert out.shape == (0, 8, 128) and sc.shape == (0, 2, 10) and ev.shape == (0, 2)
 
 
-@pytest.mark.parametrize("nsplit", [1, 5])
-def test_deterministic(nsplit):
+@pytest.mark.parametrize("nsplit,path", split_variants([1, 5]))
+def test_deterministic(nsplit, path):
     """Same inputs twice: bitwise the same O, scores and evict (no float atomics)."""
     from decode_attention_kv_05_amd import longflow as lf
     wl = W.Workload("det", B=4, Hq=32, Hkv=8, d=128, S=1000, steps=1, seed=44)
@@ -179,7 +181,7 @@ def test_deterministic(nsplit):
         dk, dv = bf16_dev(k), bf16_dev(v)
         prev = torch.full((4, 8), 7, dtype=torch.int32, device="cuda")
         out, sc, ev = lf.longflow_decode(bf16_dev(q), dk, dv, torch.from_numpy(mask).cuda(), bf16_dev(nk),
-                                         bf16_dev(nv), prev, nsplit=nsplit)
+                                         bf16_dev(nv), prev, nsplit=nsplit, split_path=path)
         torch.cuda.synchronize()
         res.append((bf16_host(out), sc.cpu().numpy(), ev.cpu().numpy()))
     for a, b in zip(*res):
@@ -217,12 +219,49 @@ def test_twins_tie_to_lowest_index():
     k[0, 0, 120] = k[0, 0, 450]
     v[0, 0, 120] = v[0, 0, 450]
     q, nk, nv = W.step_inputs(wl, 0)
-    for nsplit in (1, 2, 4):
+    for nsplit, path in split_variants((1, 2, 4)):
         out, sc, ev = lf.longflow_decode(bf16_dev(q), bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda(),
                                          bf16_dev(nk), bf16_dev(nv),
-                                         torch.full((1, 1), -1, dtype=torch.int32, device="cuda"), nsplit=nsplit)
+                                         torch.full((1, 1), -1, dtype=torch.int32, device="cuda"), nsplit=nsplit,
+                                         split_path=path)
         torch.cuda.synchronize()
         s = sc.cpu().numpy()
         assert s[0, 0, 120] == s[0, 0, 450]
         assert ev.item() == 120, (nsplit, ev.item())
         global_properties(sc, ev, torch.from_numpy(mask).cuda())
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,nsplit", [(2, 64, 8, 16384, 4), (4, 16, 4, 4096, 64), (3, 8, 2, 777, 5)])
+def test_team_path_equals_combine_path(B, Hq, Hkv, S, nsplit):
+    """The two ways of finishing a split step on the same inputs: scores and
+    evicted slots bit for bit (same logits, same pair statistics in the same
+    order, same per-slot expression), O within the O tolerance of each
+    other, the oracle on a few pairs.  The 64-split case has more pairs than
+    one round of teams holds, so the team path runs in several launches."""
+    from decode_attention_kv_05_amd import longflow as lf
+    from oracle import decode_step
+    wl = W.Workload("team_vs_combine", B=B, Hq=Hq, Hkv=Hkv, d=128, S=S, steps=1, kind="lognormal_v", seed=8200)
+    k, v, mask = W.initial_cache(wl)
+    q, nk, nv = W.step_inputs(wl, 0)
+    prev = np.full((B, Hkv), 3, dtype=np.int32)
+    res = {}
+    for path in ("team", "combine"):
+        log(f"B={B} Hq={Hq} Hkv={Hkv} S={S} nsplit={nsplit} path={path}")
+        ws = lf.new_workspace(B, Hq, Hkv, 128, S, nsplit)
+        out, sc, ev = lf.longflow_decode(bf16_dev(q), bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda(),
+                                         bf16_dev(nk), bf16_dev(nv), torch.from_numpy(prev).cuda(),
+                                         scale=float(wl.scale), workspace=ws, nsplit=nsplit, split_path=path)
+        torch.cuda.synchronize()
+        assert lf.lf_read_device_status(ws) == 0
+        res[path] = (bf16_value(bf16_host(out)), sc.cpu().numpy(), ev.cpu().numpy())
+    (ot, st, et), (oc, scb, ec) = res["team"], res["combine"]
+    assert np.array_equal(st.view(np.uint32), scb.view(np.uint32)), "scores differ between the paths"
+    assert np.array_equal(et, ec)
+    assert np.all(np.abs(ot - oc) <= 1e-2 + 1e-2 * np.abs(oc))
+    pairs = sorted({(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)})
+    o_ref, s_ref, e_ref = decode_step(q, k, v, mask, nk, nv, prev, wl.scale, pairs=pairs)
+    from gpu_util import compare_pair
+    for b, j in pairs:
+        heads = slice(j * wl.G, (j + 1) * wl.G)
+        compare_pair(ot[b, heads], st[b, j].astype(np.float64), et[b, j], o_ref[b, heads], s_ref[b, j],
+                     e_ref[b, j], mask[b] != 0, f"team b={b} j={j}")
