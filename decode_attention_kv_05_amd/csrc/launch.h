@@ -45,7 +45,7 @@ struct TopkParams {
   int Hkv, S, k, pairs;
 };
 
-// team_grid > 0: after zeroing the team exchange words, cooperative launches
+// team_grid > 0: after zeroing the team exchange words, launches (rounds)
 // of at most team_grid workgroups (whole teams of prm.nsplit, one pair per
 // team) until every pair is done; otherwise nblocks
 // workgroups of the single-split kernel or of the split kernel followed by

@@ -206,7 +206,7 @@ static int team_grid_for(int pairs, int d, int gp, int nw, size_t lds, int nspli
 }
 
 // Enqueue one step after validation: the decode kernel, and for several
-// splits either one cooperative team launch or the combine and finalize
+// splits either the team rounds or the combine and finalize
 // kernels.
 int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q, void* k_cache,
                  void* v_cache, const uint8_t* mask, uint8_t* mask_w, const void* new_k,

@@ -4,7 +4,7 @@
         [--name STEM]
     python -m decode_attention_kv_05_amd.profile_summary traffic --workload W --nsplit N \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes BYTES --command "..."
-        [--name STEM] [--kernel SUBSTRING] [--tag KEY]
+        [--name STEM] [--kernel SUBSTRING] [--tag KEY] [--dispatches-per-step N]
     python -m decode_attention_kv_05_amd.profile_summary counters DIR [DIR ...] --kernel SUBSTRING \
         --name STEM --command "..."
 
@@ -14,7 +14,8 @@ writes profiles/<STEM>_kernels.txt (STEM defaults to longflow_decode_<W>).
 (the benchmark and a plain device copy of a known size, run with `bench.py
 --copy-probe`), scales the per-dispatch KiB of the kernel whose name contains
 SUBSTRING (default: the decode kernel) by bytes-copied / KiB-counted of the
-copy, and writes profiles/<STEM>_traffic.txt plus the entry KEY (default
+copy and by the kernel's dispatches per decode call (--dispatches-per-step,
+2 for the two team rounds of a split step), and writes profiles/<STEM>_traffic.txt plus the entry KEY (default
 <W>/nsplit<N>) of profiles/traffic.json, tagged with the hash of the kernel
 sources it measured (bench.py reports the figure only while that hash
 matches).
@@ -118,8 +119,9 @@ def write_traffic(args):
     _, (cw_kib, _) = _pick(cwrite, is_copy)
     f_scale = args.copy_bytes / (cf_kib * 1024.0)
     w_scale = args.copy_bytes / (cw_kib * 1024.0)
-    read_b = f_kib * 1024.0 * f_scale
-    write_b = w_kib * 1024.0 * w_scale
+    per_step = args.dispatches_per_step
+    read_b = f_kib * 1024.0 * f_scale * per_step
+    write_b = w_kib * 1024.0 * w_scale * per_step
     total = read_b + write_b
     tag = args.tag or f"{args.workload}/nsplit{args.nsplit}"
     out = os.path.join(PROFILES, f"{args.name or 'longflow_decode_' + args.workload}_traffic.txt")
@@ -132,6 +134,8 @@ def write_traffic(args):
         f.write(f"WRITE_SIZE KiB/dispatch (mean of {nw}): {w_kib:.1f}\n")
         f.write(f"copy probe {cname[:60]}: {args.copy_bytes} bytes; FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB\n")
         f.write(f"scale factors (bytes per counted byte): fetch {f_scale:.4f}, write {w_scale:.4f}\n")
+        if per_step != 1:
+            f.write(f"dispatches of the kernel per decode call: {per_step} (rounds of the team path)\n")
         f.write(f"HBM bytes per launch: read {read_b:.0f}, write {write_b:.0f}, total {total:.0f}\n")
     path = os.path.join(PROFILES, "traffic.json")
     try:
@@ -201,6 +205,8 @@ def main():
     t.add_argument("--name", default=None)
     t.add_argument("--kernel", default=None)
     t.add_argument("--tag", default=None)
+    t.add_argument("--dispatches-per-step", type=int, default=1,
+                   help="dispatches of the kernel per decode call (team rounds); the record is per call")
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--kernel", required=True)
