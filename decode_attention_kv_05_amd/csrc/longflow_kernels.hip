@@ -780,12 +780,17 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
 
 template <int D, int GP, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_kernel(DecodeParams p) {
-  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous run of work items so neighbouring splits share an L2.
+  // Workgroups are dispatched round-robin over the 8 XCDs.  With one split
+  // per pair the pairs follow that order, so with 8 KV heads every XCD gets
+  // one head of every sequence and the same work whatever the sequences'
+  // lengths (ragged: 827.6 -> 815.7 us against contiguous runs per XCD).  The
+  // split and team modes give each XCD a contiguous run of work items, so
+  // the splits of a pair share an L2.
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int per = nblk >> 3, rem = nblk & 7;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
+  const int item = MODE == kModeSingle ? (int)blockIdx.x
+                                       : xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
   const int nsplit = MODE == kModeSingle ? 1 : p.nsplit;
   const int first = item / nsplit;
   const int sp = item - first * nsplit;

@@ -329,3 +329,63 @@ def test_stack_workspace_size():
         nq = (Hq + 2 * Hkv) * 128
         chunks |= {2 * (H // 256) // ksplit(nq, H), 2 * (Hq * 128 // 256) // ksplit(H, Hq * 128)}
     assert chunks == {2, 4, 6, 8, 10, 12, 14, 16}
+
+
+_LAYOUT_CHECK = r"""
+#include <cstdio>
+#include <cstdlib>
+#include "layout.h"
+// Every workspace region of a split step lies inside the workspace, is
+// aligned for its element type and overlaps no other region; the team
+// region holds exactly its words and the fill of zero_words covers it.
+int main() {
+  int bad = 0, cases = 0;
+  const int Bs[] = {1, 2, 3, 16, 128, 257}, Hkvs[] = {1, 2, 8}, gs[] = {1, 2, 3, 4, 8}, ds[] = {64, 128};
+  const int Ss[] = {1, 7, 256, 777, 3200, 16384, 65536}, ns[] = {2, 3, 4, 5, 16, 64, 1024};
+  for (int B : Bs) for (int Hkv : Hkvs) for (int g : gs) for (int d : ds) for (int S : Ss) for (int n : ns) {
+    if (n > S) continue;
+    int len, eff;
+    lf::split_geometry(S, n, &len, &eff);
+    if (eff < 2) continue;
+    const int gp = lf::padded_group(g);
+    const lf::WorkspaceLayout w = lf::workspace_layout(B, Hkv, d, S, gp, eff);
+    const lf::TeamLayout t = lf::team_layout(w, B, Hkv, d, gp, eff);
+    const size_t pairs = (size_t)B * Hkv;
+    struct R { size_t off, bytes, align; } r[] = {
+      {w.part_ml, pairs * eff * gp * 2 * 4, 4}, {w.part_o, pairs * eff * gp * (size_t)d * 4, 4},
+      {w.logit, pairs * (size_t)S * gp * 4, 16}, {w.vnorm, pairs * (size_t)S * 4, 4},
+      {w.cand, pairs * (size_t)lf::combine_chunks(S) * 8, 8}, {w.ffree, pairs * (size_t)lf::combine_chunks(S) * 4, 4},
+      {w.team, lf::team_region_bytes(pairs, eff, gp, d), 8}};
+    const int nr = sizeof(r) / sizeof(r[0]);
+    ++cases;
+    for (int i = 0; i < nr; ++i) {
+      if (r[i].off < 256 || r[i].off + r[i].bytes > w.total || r[i].off % r[i].align) ++bad;
+      for (int k = i + 1; k < nr; ++k)
+        if (r[i].off < r[k].off + r[k].bytes && r[k].off < r[i].off + r[i].bytes) ++bad;
+    }
+    if (t.xstat != w.team || t.xfin != t.xstat + pairs * eff * gp * 16 || t.xo != t.xfin + pairs * eff * 24 ||
+        t.xcnt != t.xo + pairs * eff * gp * (size_t)d * 8 || t.xcnt + pairs * 4 != w.team + t.zero_words * 4 ||
+        t.xo % 8 || t.xcnt % 4 || t.zero_words * 4 != lf::team_region_bytes(pairs, eff, gp, d))
+      ++bad;
+  }
+  printf("%d %d\n", cases, bad);
+  return 0;
+}
+"""
+
+
+def test_workspace_regions_fit_and_do_not_overlap(tmp_path):
+    """Host C++ check of the workspace layout of split steps (combine and
+    team regions) over a grid of shapes and split counts."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    src = tmp_path / "layout_check.cpp"
+    src.write_text(_LAYOUT_CHECK)
+    exe = tmp_path / "layout_check"
+    csrc = os.path.join(os.path.dirname(INCLUDE), "decode_attention_kv_05_amd", "csrc")
+    subprocess.run([gxx, "-std=c++17", "-O1", "-I", csrc, str(src), "-o", str(exe)], check=True)
+    cases, bad = map(int, subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split())
+    assert cases > 1000 and bad == 0, (cases, bad)
