@@ -130,3 +130,60 @@ def test_random_topk_exact(case):
     torch.cuda.synchronize()
     want = evict_topk(scores, (mask != 0)[:, None, :], k)  # [B, Hkv, k]
     assert np.array_equal(got.cpu().numpy(), np.moveaxis(want, -1, 0))
+
+
+def _path_cases():
+    rng = np.random.default_rng(20261205)
+    cases = []
+    for i in range(24):
+        G = int(rng.integers(1, 9))
+        Hkv = int(rng.integers(1, 9))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 40))
+        S = max(2, int(np.exp(rng.uniform(np.log(2.0), np.log(20000.0)))))
+        nsplit = int(min(S, rng.choice([2, 3, 4, 6, 9, 17, 64])))
+        kind = str(rng.choice(W.KINDS))
+        holes = float(rng.choice([0.0, 0.0, 0.5, 0.02]))
+        if holes and kind == "ragged":
+            kind = "plain"
+        cases.append((i, B, G, Hkv, d, S, nsplit, kind, holes))
+    return cases
+
+
+@pytest.mark.parametrize("case", _path_cases(), ids=lambda c: f"p{c[0]}")
+def test_random_team_equals_combine(case):
+    """The team and the combine path on the same random inputs: scores and
+    evicted slots bit for bit, O within the O tolerance of each other, the
+    written cache rows equal, no device status bit.  Batch sizes up to 39
+    with up to 8 KV heads and up to 64 splits reach several team rounds."""
+    from decode_attention_kv_05_amd import longflow as lf
+    from gpu_util import bf16_dev, bf16_host, bf16_value
+    i, B, G, Hkv, d, S, nsplit, kind, holes = case
+    log(f"random paths {i}: B={B} G={G} Hkv={Hkv} d={d} S={S} nsplit={nsplit} {kind} holes={holes}")
+    wl = W.Workload(f"rpath{i}", B=B, Hq=G * Hkv, Hkv=Hkv, d=d, S=S, steps=1, kind=kind, seed=35000 + i,
+                    len_lo=min(S, 1 + S // 4))
+    k, v, mask = W.initial_cache(wl)
+    if holes:
+        mask = W.holed_mask(wl, 1.0 - holes)
+        W.poison_free(k, v, mask)
+    q, nk, nv = W.step_inputs(wl, 0)
+    rng = np.random.default_rng(36000 + i)
+    prev = np.where(rng.random((B, Hkv)) < 0.8, rng.integers(0, S, (B, Hkv)), -1).astype(np.int32)
+    prev[mask[np.arange(B)[:, None], np.maximum(prev, 0)] == 0] = -1  # written slots are valid ones
+    res = {}
+    for path in ("team", "combine"):
+        ws = lf.new_workspace(B, wl.Hq, Hkv, d, S, nsplit)
+        dk, dv = bf16_dev(k), bf16_dev(v)
+        out, sc, ev = lf.longflow_decode(bf16_dev(q), dk, dv, torch.from_numpy(mask).cuda(), bf16_dev(nk),
+                                         bf16_dev(nv), torch.from_numpy(prev).cuda(), scale=float(wl.scale),
+                                         workspace=ws, nsplit=nsplit, split_path=path)
+        torch.cuda.synchronize()
+        assert lf.lf_read_device_status(ws) == 0
+        res[path] = (bf16_value(bf16_host(out)), sc.cpu().numpy(), ev.cpu().numpy(), bf16_host(dk), bf16_host(dv))
+    (ot, st, et, kt, vt), (oc, scb, ec, kc, vc) = res["team"], res["combine"]
+    assert np.array_equal(st.view(np.uint32), scb.view(np.uint32)), "scores differ between the paths"
+    assert np.array_equal(et, ec)
+    assert np.array_equal(kt, kc) and np.array_equal(vt, vc)
+    fin = np.isfinite(oc)
+    assert np.array_equal(fin, np.isfinite(ot))
+    assert np.all(np.abs(ot[fin] - oc[fin]) <= 1e-2 + 1e-2 * np.abs(oc[fin]))
