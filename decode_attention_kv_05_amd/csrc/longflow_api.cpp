@@ -68,12 +68,13 @@ int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nspli
   // The logits of a split must fit the LDS budget.
   const int64_t need = ((int64_t)S + lf::max_split_len(d, gp) - 1) / lf::max_split_len(d, gp);
   int64_t n = need;
-  // One workgroup per pair keeps the whole step on chip (no workspace round
-  // trip, no combine launch); use it when there are enough pairs to give
+  // One workgroup per pair keeps the whole step in one workgroup (no
+  // exchange between splits); use it when there are enough pairs to give
   // every compute unit work.  Otherwise split the slots until there are
   // about two workgroups per compute unit, but not below 256 slots a split.
-  // (Smaller splits that let two workgroups share a CU measured no faster
-  // for the 16384-slot GQA-8 cache: the workspace round trip dominates.)
+  // (Smaller splits that let two workgroups share a CU measured slower for
+  // the 16384-slot GQA-8 cache on both split paths: team 261 us with 8
+  // splits against 243 us with 4, combine 284 against 270.)
   if (!(need == 1 && pairs >= num_cus)) {
     const int64_t target = (2LL * num_cus + pairs - 1) / pairs;
     const int64_t cap = ((int64_t)S + 255) / 256;

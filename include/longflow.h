@@ -124,8 +124,9 @@ int lf_check_shape(int B, int Hq, int Hkv, int d, int S);
 /* Host-only choice of the number of slot splits per (sequence, KV head) for
  * a device with `num_cus` compute units.  Writes the count to *nsplit.  A
  * split count of 1 keeps the whole step of a (b, j) pair in one workgroup;
- * larger counts split the slots (flash-decoding) and add a combine kernel
- * that rescales the partial softmax statistics to the true softmax. */
+ * larger counts split the slots (flash-decoding), and the partial softmax
+ * statistics are rescaled to the true softmax either inside the step (team
+ * path) or by a combine kernel (see longflow_decode_ex). */
 int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nsplit);
 
 /* Host-only workspace size in bytes for an explicit split count (>= 1). */
