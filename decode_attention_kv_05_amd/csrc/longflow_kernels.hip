@@ -27,11 +27,17 @@
 //   finish   single split: score_i = |v_i|_1 * sum_h e_hi / L_h is written in
 //            phase V, O = acc / L, and the argmin over packed (score bits,
 //            slot) words gives the evicted slot.
-//            several splits: each split writes its (M, L, acc) partials, the
-//            logits and |v|_1 to the workspace; the combine and finalize
-//            kernels launched right after on the same stream rescale them
-//            to the true softmax.  The kernel boundary orders the two, so no cross-
-//            workgroup fences are needed.
+//            team (several splits, the default): the splits of a pair run
+//            at once; between the softmax pass and phase V they exchange
+//            their (M, L) through the workspace, so e, the scores and the
+//            argmin candidates are formed against the pair's softmax as with
+//            one split, and the last split of the pair to finish sums the
+//            O accumulators and takes the minimum.
+//            combine (several splits): each split writes its (M, L, acc)
+//            partials, the logits and |v|_1 to the workspace; the combine and
+//            finalize kernels launched right after on the same stream rescale
+//            them to the true softmax.  The kernel boundary orders the two,
+//            so no cross-workgroup fences are needed.
 //
 // Every slot goes through the same instruction sequence, so two slots with
 // identical K/V rows get bit-identical scores and the lowest-index rule
