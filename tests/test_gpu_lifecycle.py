@@ -259,3 +259,22 @@ def test_fill_step_full_size(name, len_lo, sample):
             compare_pair(o_gpu[b, heads], s_gpu[j], n_gpu[b, j], o_ref[r, heads], s_ref[r, j], n_ref[r, j],
                          m_ref[r] != 0, f"{wl.name} b={b} j={j}")
     log(f"  {wl.name}: sequences {sample} match; mask and free-slot choices exact for all {wl.B}")
+
+
+@pytest.mark.parametrize("path", ["team", "combine"])
+def test_fill_several_team_rounds(path):
+    """160 pairs with 17 splits each: the team path needs several launch
+    rounds, whose size is not a multiple of the 4 KV heads, so a sequence's
+    heads can fall in different rounds while its mask fills; lockstep with
+    the oracle from scattered free slots to full and on into eviction."""
+    wl = W.Workload("fill_rounds", B=40, Hq=16, Hkv=4, d=64, S=600, steps=1, kind="plain", seed=9800)
+    k, v, _ = W.initial_cache(wl)
+    mask = W.holed_mask(wl, 1.0 - 6.0 / 600)
+    W.poison_free(k, v, mask)
+    prev = np.repeat(lowest_free(mask)[:, None], wl.Hkv, axis=1)
+    log(f"fill over several team rounds, path={path}, free={[(m == 0).sum() for m in mask][:8]}...")
+    ls = FillLockstep(wl, k, v, mask, prev, nsplit=17, split_path=path)
+    for _ in range(int((mask == 0).sum(axis=1).max()) + 2):
+        ls.step()
+    assert ls.mask.all()
+    ls.finish()
