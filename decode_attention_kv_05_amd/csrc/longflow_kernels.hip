@@ -236,8 +236,9 @@ constexpr float kInf = __builtin_huge_valf();
 #ifndef LF_PV_DOT2
 #define LF_PV_DOT2 0
 #endif
-// Stagger of the streaming order in the split kernel: each wave starts at
-// batch (workgroup index * LF_ROTATE) mod (its batch count); 0 = in order.
+// Stagger of the streaming order in the split and team modes: each wave
+// starts at batch (workgroup index * LF_ROTATE) mod (its batch count);
+// 0 = in order.
 // Splits of a power-of-two number of rows otherwise stream in lockstep from
 // addresses a power of two apart (long_reasoning: 269.8 -> 248.6 us/step);
 // the single-split kernel measured no better staggered (ragged 3% slower).

@@ -147,7 +147,10 @@ class Lockstep:
         return out, sc, ev
 
     def check_full_cache(self):
-        """The GPU cache equals the oracle's cache bitwise for the checked sequences."""
+        """The GPU cache equals the oracle's cache bitwise for the checked
+        sequences, and no step set a device status bit (bad or masked
+        prev_slot, diverged fill, team wait out of budget)."""
+        assert self.lf.lf_read_device_status(self.ws) == 0
         for b in sorted({b for b, _ in self.pairs}):
             for j in range(self.wl.Hkv):
                 if (b, j) not in self.pairs:
