@@ -30,9 +30,9 @@ struct DecodeParams {
   uint64_t* xfin;         // team: [pairs][nsplit][3] published minimum (high, low word), lowest free slot
   uint64_t* xo;           // team: [pairs][nsplit][GP][d] published O accumulators
   uint32_t* xcnt;         // team: [pairs] splits finished
+  uint32_t* xticket;      // team: work items handed out (pair * nsplit + split)
   size_t team_words;      // team: 32-bit words of the region above, zeroed before the launch
   int pairs;              // B * Hkv
-  int pair0;              // team: first pair of this launch's round
   int Hq, Hkv, G, S, nsplit, split_len;
   int fill;               // 1: fill step (next slot = lowest free slot while any)
   float qscale;           // logit scale times log2(e)
@@ -45,11 +45,10 @@ struct TopkParams {
   int Hkv, S, k, pairs;
 };
 
-// team_grid > 0: after zeroing the team exchange words, launches (rounds)
-// of at most team_grid workgroups (whole teams of prm.nsplit, one pair per
-// team) until every pair is done; otherwise nblocks
-// workgroups of the single-split kernel or of the split kernel followed by
-// the combine and finalize kernels.
+// team_grid > 0: after zeroing the team exchange words, one launch of the
+// team kernel with one workgroup per (pair, split), nblocks in all;
+// otherwise nblocks workgroups of the single-split kernel or of the split
+// kernel followed by the combine and finalize kernels.
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
                          int team_grid, hipStream_t stream);
 // Workgroups of the team kernel for (d, gp, nw, lds) that one compute unit

@@ -36,6 +36,10 @@ constexpr int kMaxGroup = 8;          // query heads per KV head supported
 
 constexpr int kMaxWaves = LF_WAVES_LARGE_LDS > LF_WAVES_SMALL_LDS ? LF_WAVES_LARGE_LDS : LF_WAVES_SMALL_LDS;
 constexpr int kMaxSplits = 1024;      // slot splits per (sequence, KV head)
+// Largest split count the team path takes: every split of a team reads the
+// (max, sum) words of all the others, so the exchange grows with the square
+// of the count; beyond this the combine path finishes the step.
+constexpr int kMaxTeamSplits = 64;
 // LDS bytes a workgroup may spend on the logits of its slot range.
 #ifndef LF_LOGIT_LDS_KB
 #define LF_LOGIT_LDS_KB 136
@@ -72,9 +76,10 @@ struct WorkspaceLayout {
 
 // Exchange region of the team path.  Every word is a 64-bit (ready bit,
 // 32-bit payload) pair written once per step, so the region is zeroed before
-// each team launch; the counters come last.
+// each team launch; the counters (one per pair, then the ticket counter)
+// come last.
 LF_HD inline size_t team_region_bytes(size_t pairs, int nsplit_eff, int gp, int d) {
-  return pairs * nsplit_eff * ((size_t)gp * 2 + 3 + (size_t)gp * d) * 8 + pairs * 4;
+  return pairs * nsplit_eff * ((size_t)gp * 2 + 3 + (size_t)gp * d) * 8 + pairs * 4 + 4;
 }
 
 // Slots per workgroup of the split combine.
@@ -110,12 +115,14 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
 
 // Words of the team region, in this order: published split (max, sum) per
 // head, published split results (minimum candidate high and low words, lowest
-// free slot), published split O accumulators, then the arrival counters.
+// free slot), published split O accumulators, the arrival counters, and the
+// ticket counter that hands out (pair, split) work items.
 struct TeamLayout {
   size_t xstat;   // uint64 [pairs][nsplit][GP][2]
   size_t xfin;    // uint64 [pairs][nsplit][3]
   size_t xo;      // uint64 [pairs][nsplit][GP][d]
   size_t xcnt;    // uint32 [pairs]
+  size_t xticket; // uint32
   size_t zero_words;  // uint32 words of the whole region
 };
 
@@ -127,6 +134,7 @@ LF_HD inline TeamLayout team_layout(const WorkspaceLayout& w, int B, int Hkv, in
   t.xfin = t.xstat + per * gp * 2 * 8;
   t.xo = t.xfin + per * 3 * 8;
   t.xcnt = t.xo + per * gp * (size_t)d * 8;
+  t.xticket = t.xcnt + pairs * 4;
   t.zero_words = team_region_bytes(pairs, nsplit_eff, gp, d) / 4;
   return t;
 }
@@ -140,6 +148,9 @@ struct LdsLayout {
 };
 
 constexpr size_t kScratchBytes = 1024;
+// Offset in the scratch area of the team kernel's work-item ticket; the
+// decode body's reductions use the bytes below it.
+constexpr size_t kTicketSlot = kScratchBytes - 16;
 // Rows past the end of a split that a wave batch may touch; the mask and
 // logit arrays are padded by this much so those reads need no bounds check.
 constexpr int kRowPad = 128;

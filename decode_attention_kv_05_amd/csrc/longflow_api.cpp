@@ -193,22 +193,20 @@ int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void*
 
 namespace lf {
 
-// Workgroups of one team round for this step (whole teams, no more than
-// the device holds at once), or 0 when the device cannot hold a team.
-static int team_grid_for(int pairs, int d, int gp, int nw, size_t lds, int nsplit_eff) {
-  if (nsplit_eff < 2) return 0;
+// Whether the device holds a whole team (nsplit workgroups of the team
+// kernel) at once, which is all the team path needs: its workgroups take
+// (pair, split) tickets in the order they start, so every team but the one
+// holding the newest ticket is already running.
+static bool device_holds_team(int d, int gp, int nw, size_t lds, int nsplit_eff) {
+  if (nsplit_eff < 2 || nsplit_eff > lf::kMaxTeamSplits) return false;
   int per_cu = 0, cus = 0;
-  if (lf_device_num_cus(&cus) != LF_OK) return 0;
-  if (lf::team_blocks_per_cu(d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return 0;
-  const int64_t resident = (int64_t)per_cu * cus;
-  int64_t teams = resident / nsplit_eff;
-  if (teams > pairs) teams = pairs;
-  return (int)(teams * nsplit_eff);
+  if (lf_device_num_cus(&cus) != LF_OK) return false;
+  if (lf::team_blocks_per_cu(d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return false;
+  return (int64_t)per_cu * cus >= nsplit_eff;
 }
 
 // Enqueue one step after validation: the decode kernel, and for several
-// splits either the team rounds or the combine and finalize
-// kernels.
+// splits either the team launch or the combine and finalize kernels.
 int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q, void* k_cache,
                  void* v_cache, const uint8_t* mask, uint8_t* mask_w, const void* new_k,
                  const void* new_v, const int32_t* prev_slot, void* out, float* scores,
@@ -256,12 +254,13 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
   int team_grid = 0;
   if (eff > 1 && split_path != LF_SPLIT_COMBINE) {
     const lf::TeamLayout tl = lf::team_layout(wl, B, Hkv, d, gp, eff);
-    team_grid = team_grid_for(B * Hkv, d, gp, nw, lds, eff);
+    team_grid = device_holds_team(d, gp, nw, lds, eff) ? nblocks : 0;
     if (team_grid == 0 && split_path == LF_SPLIT_TEAM) return LF_E_NSPLIT;
     prm.xstat = reinterpret_cast<uint64_t*>(ws + tl.xstat);
     prm.xfin = reinterpret_cast<uint64_t*>(ws + tl.xfin);
     prm.xo = reinterpret_cast<uint64_t*>(ws + tl.xo);
     prm.xcnt = reinterpret_cast<uint32_t*>(ws + tl.xcnt);
+    prm.xticket = reinterpret_cast<uint32_t*>(ws + tl.xticket);
     prm.team_words = tl.zero_words;
   }
   return lf::launch_decode(prm, d, gp, nw, nblocks, lds, team_grid, static_cast<hipStream_t>(stream)) ==

@@ -290,13 +290,13 @@ constexpr int kModeSplit = 1;   // one workgroup per split; combine kernels fini
 constexpr int kModeTeam = 2;    // a team of workgroups per pair (one per split), all
                                 // resident at once, exchanges softmax statistics mid-step
 
-// Polls a thread may spend on all of its team waits of one pair (at least
-// 128 clocks each: 3.5 ms or more in all) before it stops waiting and sets
-// LF_DEV_TEAM_TIMEOUT.  The members of a team run concurrently, so a wait
-// lasts about one split's phase K at most; it runs out only if a member is
-// kept from running (another process holding compute units), and then the
-// step still ends, flagged.
-constexpr int kTeamSpinLimit = 1 << 16;
+// Time a thread may spend on all of its team waits of one pair before it
+// stops waiting and sets LF_DEV_TEAM_TIMEOUT: 0.2 s of the constant-rate
+// real-time counter (100 MHz).  A wait lasts about one split's phase K, or
+// for a team whose last members have not started, until some running
+// workgroup ends; it runs out only if a member is kept from running, and
+// then the step still ends, flagged.
+constexpr uint64_t kTeamWaitTicks = 20000000ull;
 constexpr uint64_t kReady = 1ull << 32;
 
 // Publishes a float as a 64-bit word whose upper half marks it written.
@@ -304,14 +304,13 @@ __device__ __forceinline__ void team_publish(uint64_t* w, float x) {
   __hip_atomic_store(w, kReady | __float_as_uint(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Waits for a word published by another workgroup of the team, drawing on
-// the thread's poll budget; once the budget is gone it returns NaN at once.
-__device__ __forceinline__ float team_wait(const uint64_t* w, uint32_t* status, int& budget) {
+// Waits for a word published by another workgroup of the team until the
+// thread's deadline; past it, it returns NaN at once.
+__device__ __forceinline__ float team_wait(const uint64_t* w, uint32_t* status, uint64_t deadline) {
   for (;;) {
     const uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v & kReady) return __uint_as_float((uint32_t)v);
-    if (budget <= 0) break;
-    --budget;
+    if (__builtin_amdgcn_s_memrealtime() > deadline) break;
     __builtin_amdgcn_s_sleep(2);
   }
   atomicOr(status, LF_DEV_TEAM_TIMEOUT);
@@ -352,6 +351,8 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   int* red_i = reinterpret_cast<int*>(best_w + NW);              // [NW]
   int* red_f = red_i + NW;                                       // [NW] fill step
   int* last = red_f + NW;                                        // team: last to finish the pair
+  static_assert(NW * GP * 4 + GP * 8 + NW * 8 + NW * 8 + 4 <= kTicketSlot,
+                "the reductions must stay below the team ticket in the scratch area");
 
   const size_t row0 = (size_t)pair * p.S;  // first cache row of this pair
   const uint16_t* krows = p.k + (row0 + s0) * D;
@@ -543,13 +544,13 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
         uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2;
         team_publish(xs + (sp * GP + tid) * 2, stat_m[tid]);
         team_publish(xs + (sp * GP + tid) * 2 + 1, l);
-        int budget = kTeamSpinLimit;
+        const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kTeamWaitTicks;
         float gm = kNegInf;
-        for (int q = 0; q < nsplit; ++q) gm = fmaxf(gm, team_wait(xs + (q * GP + tid) * 2, p.status, budget));
+        for (int q = 0; q < nsplit; ++q) gm = fmaxf(gm, team_wait(xs + (q * GP + tid) * 2, p.status, deadline));
         float gl = 0.f;
         for (int q = 0; q < nsplit; ++q) {
-          const float mq = team_wait(xs + (q * GP + tid) * 2, p.status, budget);
-          const float lq = team_wait(xs + (q * GP + tid) * 2 + 1, p.status, budget);
+          const float mq = team_wait(xs + (q * GP + tid) * 2, p.status, deadline);
+          const float lq = team_wait(xs + (q * GP + tid) * 2 + 1, p.status, deadline);
           gl += mq != kNegInf ? lq * exp2f(mq - gm) : lq;
         }
         stat_m[tid] = gm;
@@ -757,13 +758,13 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     if (tid == 0) *last = atomicAdd(p.xcnt + pair, 1u) == (unsigned)(nsplit - 1);
     __syncthreads();
     if (*last) {
-      int budget = kTeamSpinLimit;
+      const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kTeamWaitTicks;
       const uint64_t* xa = p.xo + (size_t)pair * nsplit * GP * D;
       for (int idx = tid; idx < GP * D; idx += kThreads) {
         const int h = idx / D;
         if (h >= p.G) continue;
         float o = 0.f;
-        for (int q = 0; q < nsplit; ++q) o += team_wait(xa + (size_t)q * GP * D + idx, p.status, budget);
+        for (int q = 0; q < nsplit; ++q) o += team_wait(xa + (size_t)q * GP * D + idx, p.status, deadline);
         p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] = f32_to_bf16_rne(o * stat_il[h]);
       }
       if (tid == 0) {
@@ -771,11 +772,11 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
         uint32_t ff = (uint32_t)INT_MAX;
         for (int q = 0; q < nsplit; ++q) {
           const uint64_t* xf = p.xfin + ((size_t)pair * nsplit + q) * 3;
-          const uint64_t hi = __float_as_uint(team_wait(xf, p.status, budget));
-          const uint64_t lo = __float_as_uint(team_wait(xf + 1, p.status, budget));
+          const uint64_t hi = __float_as_uint(team_wait(xf, p.status, deadline));
+          const uint64_t lo = __float_as_uint(team_wait(xf + 1, p.status, deadline));
           const uint64_t cq = hi << 32 | lo;
           m = cq < m ? cq : m;
-          ff = min(ff, __float_as_uint(team_wait(xf + 2, p.status, budget)));
+          ff = min(ff, __float_as_uint(team_wait(xf + 2, p.status, deadline)));
         }
         int32_t next = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
         if (p.fill && ff != (uint32_t)INT_MAX) next = (int32_t)ff;
@@ -791,23 +792,30 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   // per pair the pairs follow that order, so with 8 KV heads every XCD gets
   // one head of every sequence and the same work whatever the sequences'
   // lengths (ragged: 827.6 -> 815.7 us against contiguous runs per XCD).  The
-  // split and team modes give each XCD a contiguous run of work items, so
-  // the splits of a pair share an L2.
+  // split mode gives each XCD a contiguous run of work items, so the splits
+  // of a pair share an L2; the team mode takes its items from a counter.
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int per = nblk >> 3, rem = nblk & 7;
   const int item = MODE == kModeSingle ? (int)blockIdx.x
                                        : xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
   const int nsplit = MODE == kModeSingle ? 1 : p.nsplit;
-  const int first = item / nsplit;
-  const int sp = item - first * nsplit;
   if constexpr (MODE == kModeTeam) {
-    // One round of whole teams, no more than the device holds at once: team
-    // t takes pair pair0 + t.  (A persistent loop over the pairs would keep
-    // the parameters live across it and spill.)
-    decode_pair<D, GP, NW, MODE>(p, item, p.pair0 + first, sp, nsplit);
+    // Work items go out in the order workgroups start (a ticket counter,
+    // zeroed with the exchange words), not by block index: a team is then
+    // one of consecutive tickets, and every team except the one holding the
+    // newest ticket has all its members running.  At most nsplit - 1
+    // workgroups ever wait for a member that has not started, and only until
+    // any running workgroup ends, so the launch completes whenever the
+    // device holds one team at once, whatever the dispatch order.
+    extern __shared__ __align__(16) unsigned char smem[];
+    int* tk = reinterpret_cast<int*>(smem + lds_layout(D, GP, p.split_len, NW).scratch + kTicketSlot);
+    if (threadIdx.x == 0) *tk = (int)atomicAdd(p.xticket, 1u);
+    __syncthreads();
+    const int t = *tk;
+    decode_pair<D, GP, NW, MODE>(p, t, t / nsplit, t % nsplit, nsplit);
   } else {
-    decode_pair<D, GP, NW, MODE>(p, item, first, sp, nsplit);
+    decode_pair<D, GP, NW, MODE>(p, item, item / nsplit, item % nsplit, nsplit);
   }
 }
 
@@ -1018,21 +1026,12 @@ hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, int team
   if (team_grid > 0) {
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(prm.xstat), prm.team_words, 0u, stream);
     if (e != hipSuccess) return e;
-    // Rounds of at most team_grid / nsplit teams, one pair each; team_grid
-    // is what the device holds at once, so an idle device runs a round's
-    // workgroups together.  (A cooperative launch would promise it, but
-    // costs 11-19 us more per launch than a plain one.)
-    const int teams = team_grid / prm.nsplit;
-    for (int p0 = 0; p0 < prm.pairs; p0 += teams) {
-      DecodeParams arg = prm;
-      arg.pair0 = p0;
-      const int nt = prm.pairs - p0 < teams ? prm.pairs - p0 : teams;
-      hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeTeam>), dim3(nt * prm.nsplit), dim3(NW * 64),
-                         lds, stream, arg);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    // One plain launch of every (pair, split): the ticket order (see the
+    // kernel) needs no co-residency promise, so no cooperative launch (which
+    // cost 11-19 us more per launch) and no rounds.
+    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeTeam>), dim3(team_grid), dim3(NW * 64), lds,
+                       stream, prm);
+    return hipGetLastError();
   }
   if (prm.nsplit > 1) {
     hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeSplit>), dim3(nblocks), dim3(NW * 64), lds,

@@ -92,15 +92,15 @@ typedef enum lf_status {
 #define LF_DEV_WRITE_MASKED 0x2u /* prev_slot named a masked slot: written, unused */
 #define LF_DEV_FILL_DIVERGED 0x4u /* fill step: the KV heads of a sequence did not all
                                      write the same free slot (see longflow_decode_fill) */
-#define LF_DEV_TEAM_TIMEOUT 0x8u  /* team path: a split waited too long for the
-                                     other splits of its pair, which happens only
-                                     when they were kept from running at the same
-                                     time (another process holding compute units);
-                                     that step's results are unspecified */
+#define LF_DEV_TEAM_TIMEOUT 0x8u  /* team path: a split waited more than 0.2 s for
+                                     the other splits of its pair, which happens only
+                                     when they were kept from running (another
+                                     process holding compute units); that step's
+                                     results are unspecified */
 
 /* How a step with several slot splits per (b, j) pair is finished. */
-#define LF_SPLIT_AUTO 0    /* LF_SPLIT_TEAM when the device can hold a team, else
-                              LF_SPLIT_COMBINE */
+#define LF_SPLIT_AUTO 0    /* LF_SPLIT_TEAM for up to 64 splits when the device
+                              can hold a team, else LF_SPLIT_COMBINE */
 #define LF_SPLIT_COMBINE 1 /* each split writes its logits, |v|_1 and partial
                               softmax statistics to the workspace; a combine and
                               a finalize kernel rescale them to the true softmax */
@@ -109,8 +109,9 @@ typedef enum lf_status {
                               workspace mid-step, and score their slots against
                               the pair's softmax with the logits kept on chip;
                               the last split of a pair to finish writes O and
-                              the evicted slot.  Launched in rounds of whole
-                              teams no larger than the device holds at once */
+                              the evicted slot.  Workgroups take (pair, split)
+                              tickets in the order they start, so the step
+                              completes whenever the device holds one team */
 
 /* ABI version (LF_ABI_VERSION). */
 int lf_version(void);
@@ -200,16 +201,16 @@ int longflow_decode_fill(int B, int Hq, int Hkv, int d, int S, float scale,
  *   nsplit      0 = the count lf_plan_nsplit chooses for the current device
  *   split_path  LF_SPLIT_AUTO, LF_SPLIT_COMBINE or LF_SPLIT_TEAM: how a step
  *               with nsplit > 1 is finished (ignored when nsplit = 1).
- *               LF_SPLIT_TEAM returns LF_E_NSPLIT when the device cannot hold
- *               a whole team of nsplit workgroups at once.
+ *               LF_SPLIT_TEAM returns LF_E_NSPLIT for more than 64 splits
+ *               or when the device cannot hold a whole team of nsplit
+ *               workgroups at once.
  * Both paths compute the same operator (Figure 2: the split is the
  * flash-decoding form of one attention pass; abstract: attention, scoring and
  * eviction fused in one operator).  The team path reads K and V once and
  * keeps the logits on chip; the scores are those of the combine path, O may
- * differ by rounding.  The team path needs every workgroup of a round
- * running at once, which an otherwise idle device provides; where another
- * process shares the compute units, use LF_SPLIT_COMBINE (the team path
- * then may set LF_DEV_TEAM_TIMEOUT).  Same workspace size as
+ * differ by rounding.  A team's splits wait for each other mid-step (at
+ * most 0.2 s, else LF_DEV_TEAM_TIMEOUT); where another process may hold
+ * compute units for that long, use LF_SPLIT_COMBINE.  Same workspace size as
  * longflow_decode_nsplit. */
 int longflow_decode_ex(int B, int Hq, int Hkv, int d, int S, float scale,
                        const void* q, void* k_cache, void* v_cache, uint8_t* mask,

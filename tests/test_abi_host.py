@@ -223,7 +223,7 @@ def test_fill_workspace_has_free_slot_minima():
     """Split workspaces hold one 32-bit lowest-free-slot word per combine chunk,
     then the team path's exchange region: per split of a pair 64-bit words for
     its (max, sum) per padded head, its three results and its O accumulators,
-    and one 32-bit counter per pair."""
+    one 32-bit counter per pair and the 32-bit ticket counter."""
     B, Hq, Hkv, d, S = 4, 16, 2, 128, 5000
     one = lf.lf_workspace_size(B, Hq, Hkv, d, S, 1)
     assert one == 256
@@ -233,7 +233,7 @@ def test_fill_workspace_has_free_slot_minima():
     split = 3
     expect = 256
     for n in (pairs * split * gp * 2 * 4, pairs * split * gp * d * 4, pairs * S * gp * 4, pairs * S * 4,
-              pairs * chunks * 8, pairs * chunks * 4, pairs * split * (gp * 2 + 3 + gp * d) * 8 + pairs * 4):
+              pairs * chunks * 8, pairs * chunks * 4, pairs * split * (gp * 2 + 3 + gp * d) * 8 + pairs * 4 + 4):
         expect += -(-n // 256) * 256
     assert lf.lf_workspace_size(B, Hq, Hkv, d, S, split) == expect
 
@@ -364,8 +364,9 @@ int main() {
         if (r[i].off < r[k].off + r[k].bytes && r[k].off < r[i].off + r[i].bytes) ++bad;
     }
     if (t.xstat != w.team || t.xfin != t.xstat + pairs * eff * gp * 16 || t.xo != t.xfin + pairs * eff * 24 ||
-        t.xcnt != t.xo + pairs * eff * gp * (size_t)d * 8 || t.xcnt + pairs * 4 != w.team + t.zero_words * 4 ||
-        t.xo % 8 || t.xcnt % 4 || t.zero_words * 4 != lf::team_region_bytes(pairs, eff, gp, d))
+        t.xcnt != t.xo + pairs * eff * gp * (size_t)d * 8 || t.xticket != t.xcnt + pairs * 4 ||
+        t.xticket + 4 != w.team + t.zero_words * 4 || t.xo % 8 || t.xcnt % 4 ||
+        t.zero_words * 4 != lf::team_region_bytes(pairs, eff, gp, d))
       ++bad;
   }
   printf("%d %d\n", cases, bad);

@@ -263,10 +263,10 @@ def test_fill_step_full_size(name, len_lo, sample):
 
 @pytest.mark.parametrize("path", ["team", "combine"])
 def test_fill_several_team_rounds(path):
-    """160 pairs with 17 splits each: the team path needs several launch
-    rounds, whose size is not a multiple of the 4 KV heads, so a sequence's
-    heads can fall in different rounds while its mask fills; lockstep with
-    the oracle from scattered free slots to full and on into eviction."""
+    """160 pairs with 17 splits each: more teams than the device holds at
+    once (about 30), so the KV heads of a sequence run at different times
+    while its mask fills; lockstep with the oracle from scattered free slots
+    to full and on into eviction."""
     wl = W.Workload("fill_rounds", B=40, Hq=16, Hkv=4, d=64, S=600, steps=1, kind="plain", seed=9800)
     k, v, _ = W.initial_cache(wl)
     mask = W.holed_mask(wl, 1.0 - 6.0 / 600)

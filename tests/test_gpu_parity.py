@@ -236,8 +236,8 @@ def test_team_path_equals_combine_path(B, Hq, Hkv, S, nsplit):
     """The two ways of finishing a split step on the same inputs: scores and
     evicted slots bit for bit (same logits, same pair statistics in the same
     order, same per-slot expression), O within the O tolerance of each
-    other, the oracle on a few pairs.  The 64-split case has more pairs than
-    one round of teams holds, so the team path runs in several launches."""
+    other, the oracle on a few pairs.  The 64-split case has more teams than
+    the device holds at once, so later teams start as earlier ones end."""
     from decode_attention_kv_05_amd import longflow as lf
     from oracle import decode_step
     wl = W.Workload("team_vs_combine", B=B, Hq=Hq, Hkv=Hkv, d=128, S=S, steps=1, kind="lognormal_v", seed=8200)

@@ -155,7 +155,8 @@ def test_random_team_equals_combine(case):
     """The team and the combine path on the same random inputs: scores and
     evicted slots bit for bit, O within the O tolerance of each other, the
     written cache rows equal, no device status bit.  Batch sizes up to 39
-    with up to 8 KV heads and up to 64 splits reach several team rounds."""
+    with up to 8 KV heads and up to 64 splits give more teams than the
+    device holds at once."""
     from decode_attention_kv_05_amd import longflow as lf
     from gpu_util import bf16_dev, bf16_host, bf16_value
     i, B, G, Hkv, d, S, nsplit, kind, holes = case
