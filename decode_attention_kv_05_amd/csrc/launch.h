@@ -30,7 +30,7 @@ struct DecodeParams {
   uint64_t* xfin;         // team: [pairs][nsplit][3] published minimum (high, low word), lowest free slot
   uint64_t* xo;           // team: [pairs][nsplit][GP][d] published O accumulators
   uint32_t* xcnt;         // team: [pairs] splits finished
-  uint32_t* xticket;      // team: work items handed out (pair * nsplit + split)
+  uint32_t* xticket;      // team: [kTicketRanges] work items handed out per range
   size_t team_words;      // team: 32-bit words of the region above, zeroed before the launch
   int pairs;              // B * Hkv
   int Hq, Hkv, G, S, nsplit, split_len;

@@ -40,6 +40,12 @@ constexpr int kMaxSplits = 1024;      // slot splits per (sequence, KV head)
 // (max, sum) words of all the others, so the exchange grows with the square
 // of the count; beyond this the combine path finishes the step.
 constexpr int kMaxTeamSplits = 64;
+// Ticket counters of the team path; range r holds pairs
+// [ticket_range_first_pair(pairs, r), ticket_range_first_pair(pairs, r + 1)).
+constexpr int kTicketRanges = 8;
+LF_HD inline int ticket_range_first_pair(int pairs, int r) {
+  return (int)((long long)pairs * r / kTicketRanges);
+}
 // LDS bytes a workgroup may spend on the logits of its slot range.
 #ifndef LF_LOGIT_LDS_KB
 #define LF_LOGIT_LDS_KB 136
@@ -76,10 +82,10 @@ struct WorkspaceLayout {
 
 // Exchange region of the team path.  Every word is a 64-bit (ready bit,
 // 32-bit payload) pair written once per step, so the region is zeroed before
-// each team launch; the counters (one per pair, then the ticket counter)
+// each team launch; the counters (one per pair, then the ticket counters)
 // come last.
 LF_HD inline size_t team_region_bytes(size_t pairs, int nsplit_eff, int gp, int d) {
-  return pairs * nsplit_eff * ((size_t)gp * 2 + 3 + (size_t)gp * d) * 8 + pairs * 4 + 4;
+  return pairs * nsplit_eff * ((size_t)gp * 2 + 3 + (size_t)gp * d) * 8 + pairs * 4 + kTicketRanges * 4;
 }
 
 // Slots per workgroup of the split combine.
@@ -116,13 +122,13 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
 // Words of the team region, in this order: published split (max, sum) per
 // head, published split results (minimum candidate high and low words, lowest
 // free slot), published split O accumulators, the arrival counters, and the
-// ticket counter that hands out (pair, split) work items.
+// ticket counters that hand out (pair, split) work items.
 struct TeamLayout {
   size_t xstat;   // uint64 [pairs][nsplit][GP][2]
   size_t xfin;    // uint64 [pairs][nsplit][3]
   size_t xo;      // uint64 [pairs][nsplit][GP][d]
   size_t xcnt;    // uint32 [pairs]
-  size_t xticket; // uint32
+  size_t xticket; // uint32 [kTicketRanges]
   size_t zero_words;  // uint32 words of the whole region
 };
 

@@ -193,16 +193,16 @@ int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void*
 
 namespace lf {
 
-// Whether the device holds a whole team (nsplit workgroups of the team
-// kernel) at once, which is all the team path needs: its workgroups take
-// (pair, split) tickets in the order they start, so every team but the one
-// holding the newest ticket is already running.
-static bool device_holds_team(int d, int gp, int nw, size_t lds, int nsplit_eff) {
+// Whether the device holds more team-kernel workgroups at once than can
+// ever be waiting, which is all the team path needs: its workgroups take
+// (pair, split) tickets in the order they start, so in each ticket range
+// every team but the one holding the newest ticket is already running.
+static bool device_holds_teams(int d, int gp, int nw, size_t lds, int nsplit_eff) {
   if (nsplit_eff < 2 || nsplit_eff > lf::kMaxTeamSplits) return false;
   int per_cu = 0, cus = 0;
   if (lf_device_num_cus(&cus) != LF_OK) return false;
   if (lf::team_blocks_per_cu(d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return false;
-  return (int64_t)per_cu * cus >= nsplit_eff;
+  return (int64_t)per_cu * cus > (int64_t)lf::kTicketRanges * (nsplit_eff - 1);
 }
 
 // Enqueue one step after validation: the decode kernel, and for several
@@ -254,7 +254,7 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
   int team_grid = 0;
   if (eff > 1 && split_path != LF_SPLIT_COMBINE) {
     const lf::TeamLayout tl = lf::team_layout(wl, B, Hkv, d, gp, eff);
-    team_grid = device_holds_team(d, gp, nw, lds, eff) ? nblocks : 0;
+    team_grid = device_holds_teams(d, gp, nw, lds, eff) ? nblocks : 0;
     if (team_grid == 0 && split_path == LF_SPLIT_TEAM) return LF_E_NSPLIT;
     prm.xstat = reinterpret_cast<uint64_t*>(ws + tl.xstat);
     prm.xfin = reinterpret_cast<uint64_t*>(ws + tl.xfin);

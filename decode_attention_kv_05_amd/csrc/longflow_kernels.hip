@@ -801,18 +801,36 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
                                        : xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
   const int nsplit = MODE == kModeSingle ? 1 : p.nsplit;
   if constexpr (MODE == kModeTeam) {
-    // Work items go out in the order workgroups start (a ticket counter,
-    // zeroed with the exchange words), not by block index: a team is then
-    // one of consecutive tickets, and every team except the one holding the
-    // newest ticket has all its members running.  At most nsplit - 1
-    // workgroups ever wait for a member that has not started, and only until
-    // any running workgroup ends, so the launch completes whenever the
-    // device holds one team at once, whatever the dispatch order.
+    // Work items go out by tickets in the order workgroups start, not by
+    // block index.  The pairs form kTicketRanges ranges of whole teams, each
+    // with its own counter (zeroed with the exchange words); a workgroup
+    // claims from range (block index mod kTicketRanges) first and from the
+    // next ranges once that one is used up.  There are as many workgroups as
+    // items, so every claim succeeds.  Within a range tickets go out in start
+    // order, so every team of a range except the one holding its newest
+    // ticket has all its members running: at most kTicketRanges *
+    // (nsplit - 1) workgroups ever wait for members that have not started,
+    // and only until some running workgroup ends.  The launch completes
+    // whenever the device holds more than that at once, whatever the
+    // dispatch order.  (One counter for all made 256 workgroups queue on one
+    // atomic as a wave of them started: 3-4% slower.)
     extern __shared__ __align__(16) unsigned char smem[];
     int* tk = reinterpret_cast<int*>(smem + lds_layout(D, GP, p.split_len, NW).scratch + kTicketSlot);
-    if (threadIdx.x == 0) *tk = (int)atomicAdd(p.xticket, 1u);
+    if (threadIdx.x == 0) {
+      int claimed = -1;
+      for (int k = 0; k < kTicketRanges && claimed < 0; ++k) {
+        const int r = (int)((blockIdx.x + k) % kTicketRanges);
+        const int lo = ticket_range_first_pair(p.pairs, r) * nsplit;
+        const int hi = ticket_range_first_pair(p.pairs, r + 1) * nsplit;
+        if (lo == hi) continue;
+        const unsigned t = atomicAdd(p.xticket + r, 1u);
+        if (t < (unsigned)(hi - lo)) claimed = lo + (int)t;
+      }
+      *tk = claimed;
+    }
     __syncthreads();
     const int t = *tk;
+    if (t < 0) return;  // not reached: one workgroup per item
     decode_pair<D, GP, NW, MODE>(p, t, t / nsplit, t % nsplit, nsplit);
   } else {
     decode_pair<D, GP, NW, MODE>(p, item, item / nsplit, item % nsplit, nsplit);

@@ -111,7 +111,8 @@ typedef enum lf_status {
                               the last split of a pair to finish writes O and
                               the evicted slot.  Workgroups take (pair, split)
                               tickets in the order they start, so the step
-                              completes whenever the device holds one team */
+                              completes whenever the device holds more than
+                              8 * (nsplit - 1) of them at once */
 
 /* ABI version (LF_ABI_VERSION). */
 int lf_version(void);
@@ -202,8 +203,8 @@ int longflow_decode_fill(int B, int Hq, int Hkv, int d, int S, float scale,
  *   split_path  LF_SPLIT_AUTO, LF_SPLIT_COMBINE or LF_SPLIT_TEAM: how a step
  *               with nsplit > 1 is finished (ignored when nsplit = 1).
  *               LF_SPLIT_TEAM returns LF_E_NSPLIT for more than 64 splits
- *               or when the device cannot hold a whole team of nsplit
- *               workgroups at once.
+ *               or when the device cannot hold more than 8 * (nsplit - 1)
+ *               of its workgroups at once.
  * Both paths compute the same operator (Figure 2: the split is the
  * flash-decoding form of one attention pass; abstract: attention, scoring and
  * eviction fused in one operator).  The team path reads K and V once and

@@ -223,7 +223,7 @@ def test_fill_workspace_has_free_slot_minima():
     """Split workspaces hold one 32-bit lowest-free-slot word per combine chunk,
     then the team path's exchange region: per split of a pair 64-bit words for
     its (max, sum) per padded head, its three results and its O accumulators,
-    one 32-bit counter per pair and the 32-bit ticket counter."""
+    one 32-bit counter per pair and eight 32-bit ticket counters."""
     B, Hq, Hkv, d, S = 4, 16, 2, 128, 5000
     one = lf.lf_workspace_size(B, Hq, Hkv, d, S, 1)
     assert one == 256
@@ -233,7 +233,7 @@ def test_fill_workspace_has_free_slot_minima():
     split = 3
     expect = 256
     for n in (pairs * split * gp * 2 * 4, pairs * split * gp * d * 4, pairs * S * gp * 4, pairs * S * 4,
-              pairs * chunks * 8, pairs * chunks * 4, pairs * split * (gp * 2 + 3 + gp * d) * 8 + pairs * 4 + 4):
+              pairs * chunks * 8, pairs * chunks * 4, pairs * split * (gp * 2 + 3 + gp * d) * 8 + pairs * 4 + 8 * 4):
         expect += -(-n // 256) * 256
     assert lf.lf_workspace_size(B, Hq, Hkv, d, S, split) == expect
 
@@ -365,9 +365,14 @@ int main() {
     }
     if (t.xstat != w.team || t.xfin != t.xstat + pairs * eff * gp * 16 || t.xo != t.xfin + pairs * eff * 24 ||
         t.xcnt != t.xo + pairs * eff * gp * (size_t)d * 8 || t.xticket != t.xcnt + pairs * 4 ||
-        t.xticket + 4 != w.team + t.zero_words * 4 || t.xo % 8 || t.xcnt % 4 ||
+        t.xticket + 4 * lf::kTicketRanges != w.team + t.zero_words * 4 || t.xo % 8 || t.xcnt % 4 ||
         t.zero_words * 4 != lf::team_region_bytes(pairs, eff, gp, d))
       ++bad;
+  }
+  for (int pairs = 1; pairs < 3000; pairs += 7) {
+    if (lf::ticket_range_first_pair(pairs, 0) != 0 || lf::ticket_range_first_pair(pairs, lf::kTicketRanges) != pairs) ++bad;
+    for (int r = 0; r < lf::kTicketRanges; ++r)
+      if (lf::ticket_range_first_pair(pairs, r + 1) < lf::ticket_range_first_pair(pairs, r)) ++bad;
   }
   printf("%d %d\n", cases, bad);
   return 0;
