@@ -15,7 +15,7 @@ writes profiles/<STEM>_kernels.txt (STEM defaults to longflow_decode_<W>).
 --copy-probe`), scales the per-dispatch KiB of the kernel whose name contains
 SUBSTRING (default: the decode kernel) by bytes-copied / KiB-counted of the
 copy and by the kernel's dispatches per decode call (--dispatches-per-step,
-2 for the two team rounds of a split step), and writes profiles/<STEM>_traffic.txt plus the entry KEY (default
+default 1), and writes profiles/<STEM>_traffic.txt plus the entry KEY (default
 <W>/nsplit<N>) of profiles/traffic.json, tagged with the hash of the kernel
 sources it measured (bench.py reports the figure only while that hash
 matches).
@@ -135,7 +135,7 @@ def write_traffic(args):
         f.write(f"copy probe {cname[:60]}: {args.copy_bytes} bytes; FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB\n")
         f.write(f"scale factors (bytes per counted byte): fetch {f_scale:.4f}, write {w_scale:.4f}\n")
         if per_step != 1:
-            f.write(f"dispatches of the kernel per decode call: {per_step} (rounds of the team path)\n")
+            f.write(f"dispatches of the kernel per decode call: {per_step}\n")
         f.write(f"HBM bytes per launch: read {read_b:.0f}, write {write_b:.0f}, total {total:.0f}\n")
     path = os.path.join(PROFILES, "traffic.json")
     try:

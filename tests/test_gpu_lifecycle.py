@@ -262,17 +262,17 @@ def test_fill_step_full_size(name, len_lo, sample):
 
 
 @pytest.mark.parametrize("path", ["team", "combine"])
-def test_fill_several_team_rounds(path):
+def test_fill_more_teams_than_the_device_holds(path):
     """160 pairs with 17 splits each: more teams than the device holds at
     once (about 30), so the KV heads of a sequence run at different times
     while its mask fills; lockstep with the oracle from scattered free slots
     to full and on into eviction."""
-    wl = W.Workload("fill_rounds", B=40, Hq=16, Hkv=4, d=64, S=600, steps=1, kind="plain", seed=9800)
+    wl = W.Workload("fill_many_teams", B=40, Hq=16, Hkv=4, d=64, S=600, steps=1, kind="plain", seed=9800)
     k, v, _ = W.initial_cache(wl)
     mask = W.holed_mask(wl, 1.0 - 6.0 / 600)
     W.poison_free(k, v, mask)
     prev = np.repeat(lowest_free(mask)[:, None], wl.Hkv, axis=1)
-    log(f"fill over several team rounds, path={path}, free={[(m == 0).sum() for m in mask][:8]}...")
+    log(f"fill with more teams than the device holds, path={path}, free={[(m == 0).sum() for m in mask][:8]}...")
     ls = FillLockstep(wl, k, v, mask, prev, nsplit=17, split_path=path)
     for _ in range(int((mask == 0).sum(axis=1).max()) + 2):
         ls.step()
