@@ -206,7 +206,7 @@ def main():
     t.add_argument("--kernel", default=None)
     t.add_argument("--tag", default=None)
     t.add_argument("--dispatches-per-step", type=int, default=1,
-                   help="dispatches of the kernel per decode call (team rounds); the record is per call")
+                   help="dispatches of the kernel per decode call; the record is per call")
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--kernel", required=True)
