@@ -171,7 +171,7 @@ int enqueue_stack(const StackArgs& a, hipStream_t s) {
     float* sc = (a.scores && a.scores[l]) ? a.scores[l] : ws_scores;
     int rc = lf::enqueue_decode_step(a.B, a.Hq, a.Hkv, a.d, a.S, a.scale, q, a.k_cache[l], a.v_cache[l],
                                      a.mask[l], nullptr, kn, vn, a.slot[l], o, sc, a.slot[l],
-                                     ws + wl.dec, a.nsplit, LF_SPLIT_COMBINE, s);
+                                     ws + wl.dec, a.nsplit, LF_SPLIT_AUTO, s);
     if (rc != LF_OK) return rc;
     lf::GemmParams g2{o, static_cast<const uint16_t*>(a.w_o[l]), xin, xout, part, a.B, a.H, a.Hq * a.d, 0, 0};
     if (lf::launch_gemm(g2, s) != hipSuccess) return LF_E_HIP;

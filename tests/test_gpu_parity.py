@@ -265,3 +265,46 @@ def test_team_path_equals_combine_path(B, Hq, Hkv, S, nsplit):
         heads = slice(j * wl.G, (j + 1) * wl.G)
         compare_pair(ot[b, heads], st[b, j].astype(np.float64), et[b, j], o_ref[b, heads], s_ref[b, j],
                      e_ref[b, j], mask[b] != 0, f"team b={b} j={j}")
+
+
+def test_team_path_replays_in_a_graph():
+    """A team-path step captured in a HIP graph: five replays, each after new
+    queries are copied in (eager work between the replays), equal bit for
+    bit to an eager call on the same inputs.  The fill kernel that clears the
+    exchange words is part of the graph, so every replay starts clean."""
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("graph_team", B=2, Hq=16, Hkv=2, d=128, S=4096, steps=6, kind="lognormal_v", seed=8300)
+    k, v, mask = W.initial_cache(wl)
+    dk, dv, dm = bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda()
+    q0, nk, nv = W.step_inputs(wl, 0)
+    dq, dnk, dnv = bf16_dev(q0), bf16_dev(nk), bf16_dev(nv)
+    prev = torch.full((wl.B, wl.Hkv), -1, dtype=torch.int32, device="cuda")  # no write: the step is repeatable
+    mk = lambda: (torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device="cuda"),
+                  torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device="cuda"),
+                  torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device="cuda"))
+    og, sg, eg = mk()
+    ws_g = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, 4)
+    call = lambda o, s, e, ws: lf.longflow_decode(dq, dk, dv, dm, dnk, dnv, prev, scale=float(wl.scale), out=o,
+                                                 scores=s, evict_slot=e, workspace=ws, nsplit=4, split_path="team")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(og, sg, eg, ws_g)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(og, sg, eg, ws_g)
+    oe, se, ee = mk()
+    ws_e = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, 4)
+    for t in range(1, 6):
+        q, _, _ = W.step_inputs(wl, t)
+        dq.copy_(bf16_dev(q))
+        g.replay()
+        torch.cuda.synchronize()
+        call(oe, se, ee, ws_e)
+        torch.cuda.synchronize()
+        log(f"replay {t}")
+        assert torch.equal(og.view(torch.int16), oe.view(torch.int16))
+        assert torch.equal(sg.view(torch.int32), se.view(torch.int32)) and torch.equal(eg, ee)
+        assert lf.lf_read_device_status(ws_g) == 0
