@@ -10,9 +10,13 @@ next evicted slot for every (sequence, KV head), all in one kernel launch.
 The default workload is the Qwen3-8B-shaped layer (batch 128, 32 query / 8
 KV heads, d 128, 3200 slots, bf16 K/V).  Inputs of every step are generated
 and uploaded before timing; the evicted slots go from step to step on the
-device.  K steps are timed between one pair of events after W warm-up
-steps; K further steps, each between its own pair of events, give the
-per-launch durations behind the roofline figure.  Prints one JSON line.
+device.  After at least W warm-up steps and at least one second of them
+(clocks ramp up over the first milliseconds), K steps are timed between one
+pair of events, five times over; the median of the five is the reported
+time per step.  K further steps, each between its own pair of events, give
+per-launch durations as a second figure, and plain device copy and read
+probes on the same GPU give the box's practical HBM rates.  Prints one JSON
+line.
 
 Other modes measure the cache-lifecycle entry points on the same shape:
   fill     longflow_decode_fill on caches that start 2K + W slots short of
@@ -41,6 +45,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused decode-attn+evict: KV GB/s (% HBM peak), steps/s at B=128, 3200 slots"
 HBM_PEAK_GBPS = 8000.0
+REPEATS = 5            # timed repeats of K steps; the median is reported
+WARMUP_MIN_S = 1.0     # warm-up lasts at least this long, whatever W says
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 
@@ -87,13 +93,48 @@ def measured_traffic(tag):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
-    """The fp64 oracle, single-threaded, on a bounded sample of the same
-    workload: up to `max_pairs` (sequence, KV head) pairs per step, over
-    consecutive steps until `min_seconds` of work, scaled by valid K/V bytes
-    to whole steps."""
-    from threadpoolctl import threadpool_limits
+def host_cores():
+    """Threads the CPU baseline may use: the process's CPU share, at most 16
+    (the host share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
+
+def host_info():
+    """CPU model and the BLAS library numpy runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or "none found"
+    except Exception:
+        pass
+    return model, blas
+
+
+def _per_sequence(fn, nb, workers):
+    """fn(b) for b < nb on `workers` threads (numpy releases the GIL in its
+    array work); BLAS limited to one thread per worker."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, range(nb)))
+
+
+def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    workload: up to `max_pairs` (sequence, KV head) pairs per step, one
+    sequence per task on a thread pool, over consecutive steps until
+    `min_seconds` of wall time, scaled by valid K/V bytes to whole steps."""
     from decode_attention_kv_05_amd import workloads as W
     from oracle import decode_step
 
@@ -101,25 +142,31 @@ def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
     batch = list(range(nb))
     k, v, m = W.initial_cache(wl, batch)
     prev = W.first_prev_slot(wl, batch)
+    cores = host_cores()
     steps, busy = 0, 0.0
-    with threadpool_limits(limits=1):
-        while busy < min_seconds and steps < wl.steps:
-            q, nk, nv = W.step_inputs(wl, steps, batch)
-            t0 = time.perf_counter()
-            _, _, prev = decode_step(q, k, v, m, nk, nv, prev, wl.scale)
-            busy += time.perf_counter() - t0
-            steps += 1
+    while busy < min_seconds and steps < wl.steps:
+        q, nk, nv = W.step_inputs(wl, steps, batch)
+        t0 = time.perf_counter()
+        res = _per_sequence(lambda b: decode_step(q[b:b + 1], k[b:b + 1], v[b:b + 1], m[b:b + 1], nk[b:b + 1],
+                                                  nv[b:b + 1], prev[b:b + 1], wl.scale), nb, cores)
+        busy += time.perf_counter() - t0
+        prev = np.concatenate([r[2] for r in res])
+        steps += 1
     frac = valid_slots(m) / max(1, valid_slots(mask))
     s_per_step = busy / steps / frac
+    model, blas = host_info()
     return {
         "value": round(kv_bytes(wl, mask) / s_per_step / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{nb * wl.Hkv} of {wl.B * wl.Hkv} (sequence, KV head) pairs over {steps} decode steps "
-                  f"({busy:.1f} s), scaled by valid K/V bytes; numpy fp64, BLAS limited to 1 thread",
+                  f"({busy:.1f} s wall), scaled by valid K/V bytes; numpy fp64, one sequence per task on "
+                  f"{cores} threads, BLAS 1 thread each",
         "steps_per_s": round(1.0 / s_per_step, 6),
         "s_per_step": round(s_per_step, 3),
+        "cpu_model": model,
+        "blas": blas,
     }
 
 
@@ -150,11 +197,9 @@ def cpu_baseline_topk(B, Hkv, S, k, min_seconds=10.0):
 
 
 def cpu_baseline_fill(wl, max_pairs, fill_from, min_seconds=10.0):
-    """The oracle's fill step, single-threaded, on the first sequences of the
-    fill workload (same start state), consecutive steps until `min_seconds`,
-    scaled by valid K/V bytes to whole steps of the full batch."""
-    from threadpoolctl import threadpool_limits
-
+    """The oracle's fill step on the host cores (one sequence per task), on
+    the first sequences of the fill workload (same start state), consecutive
+    steps until `min_seconds` of wall time, as valid K/V bytes per second."""
     from decode_attention_kv_05_amd import workloads as W
     from oracle import decode_step_fill
 
@@ -164,62 +209,122 @@ def cpu_baseline_fill(wl, max_pairs, fill_from, min_seconds=10.0):
     m = (np.arange(wl.S)[None, :] < fill_from).astype(np.uint8).repeat(nb, 0)
     W.poison_free(k, v, m)
     prev = np.full((nb, wl.Hkv), min(fill_from, wl.S - 1), dtype=np.int32)
+    cores = host_cores()
     steps, busy, rows = 0, 0.0, 0
-    with threadpool_limits(limits=1):
-        while busy < min_seconds and steps < wl.steps:
-            q, nk, nv = W.step_inputs(wl, steps, batch)
-            t0 = time.perf_counter()
-            _, _, prev, m = decode_step_fill(q, k, v, m, nk, nv, prev, wl.scale)
-            busy += time.perf_counter() - t0
-            rows += int(np.count_nonzero(m))
-            steps += 1
+    while busy < min_seconds and steps < wl.steps:
+        q, nk, nv = W.step_inputs(wl, steps, batch)
+        t0 = time.perf_counter()
+        res = _per_sequence(lambda b: decode_step_fill(q[b:b + 1], k[b:b + 1], v[b:b + 1], m[b:b + 1],
+                                                       nk[b:b + 1], nv[b:b + 1], prev[b:b + 1], wl.scale),
+                            nb, cores)
+        busy += time.perf_counter() - t0
+        prev = np.concatenate([r[2] for r in res])
+        m = np.concatenate([r[3] for r in res])
+        rows += int(np.count_nonzero(m))
+        steps += 1
     kv_per_row = wl.Hkv * wl.d * 2 * 2
     rate = rows * kv_per_row / busy
+    model, blas = host_info()
     return {
         "value": round(rate / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{nb * wl.Hkv} of {wl.B * wl.Hkv} (sequence, KV head) pairs over {steps} fill steps "
-                  f"({busy:.1f} s), valid K/V bytes per second; numpy fp64, BLAS limited to 1 thread",
+                  f"({busy:.1f} s wall), valid K/V bytes per second; numpy fp64, one sequence per task on "
+                  f"{cores} threads, BLAS 1 thread each",
+        "cpu_model": model,
+        "blas": blas,
     }
 
 
-def timed(step, K, Wm, stream, dev):
-    """Warm up with steps 0 .. Wm-1, then time steps Wm .. Wm+K-1 between one
-    pair of events, synchronized on both sides.  Then run steps Wm+K ..
-    Wm+2K-1, untimed as a whole, with an event pair around each for the
-    per-launch durations: events recorded between launches hold the next
-    launch back by a few microseconds, so they stay out of the timed pass.
-    Returns (ms per timed step, per-launch ms of the second pass, wall
-    seconds of the timed pass)."""
+def timed(step, K, Wm, stream, dev, reset=None):
+    """Warm up with at least Wm steps and at least WARMUP_MIN_S seconds of
+    them; then REPEATS times: K steps between one pair of events on the
+    launch stream, synchronized on both sides.  Then K steps, untimed as a
+    whole, with an event pair around each for the per-launch durations
+    (events recorded between launches hold the next launch back by a few
+    microseconds, so they stay out of the timed repeats).  Steps are numbered
+    on from the warm-up; reset(t), if given, restores the start state before
+    every repeat and before the per-launch pass (untimed).  Returns (ms per
+    step of each repeat, per-launch ms, wall seconds of the timed repeats,
+    warm-up steps run)."""
     import torch
-    for t in range(Wm):
-        step(t)
-    torch.cuda.synchronize(dev)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for t in range(K):
-        step(Wm + t)
-    end.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
+    t = 0
+    w0 = time.perf_counter()
+    while t < Wm or time.perf_counter() - w0 < WARMUP_MIN_S:
+        for _ in range(max(1, Wm)):
+            step(t)
+            t += 1
+        torch.cuda.synchronize(dev)
+    warm = t
+    reps, wall = [], 0.0
+    for _ in range(REPEATS):
+        if reset is not None:
+            reset(t)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(K):
+            step(t)
+            t += 1
+        end.record(stream)
+        torch.cuda.synchronize(dev)
+        wall += time.perf_counter() - wall0
+        reps.append(start.elapsed_time(end) / K)
+    if reset is not None:
+        reset(t)
+        torch.cuda.synchronize(dev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    for t in range(K):
-        starts[t].record(stream)
-        step(Wm + K + t)
-        ends[t].record(stream)
+    for i in range(K):
+        starts[i].record(stream)
+        step(t)
+        t += 1
+        ends[i].record(stream)
     torch.cuda.synchronize(dev)
     per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    return total_ms / K, per_launch, wall
+    return np.array(reps), per_launch, wall, warm
 
 
-def roofline(alg_bytes_per_launch, per_launch_ms, kernel, traffic):
+def hbm_probes(dev, nbytes=1 << 30, reps=5):
+    """The GPU's practical HBM rates on this machine, from plain torch kernels
+    (not the library): a device-to-device copy of nbytes (read + write
+    bytes per second) and a read-only reduction over nbytes (read bytes per
+    second); median of `reps` event-timed runs each."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+
+    def rate(fn, moved):
+        fn()
+        torch.cuda.synchronize(dev)
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize(dev)
+            ts.append(a.elapsed_time(b) / 1e3)
+        return round(moved / float(np.median(ts)) / 1e9, 1)
+
+    out = {"copy_GBps": rate(lambda: dst.copy_(src), 2 * nbytes),
+           "read_GBps": rate(lambda: src.sum(dtype=torch.float32), nbytes),
+           "bytes": nbytes, "how": "torch copy_ and sum over 1 GiB of bf16, median of 5"}
+    del src, dst
+    return out
+
+
+def roofline(alg_bytes_per_launch, step_ms, per_launch_ms, kernel, traffic):
+    """HBM roofline of the dominant kernel.  achieved: algorithmic bytes per
+    step over the median timed step (one decode launch per step);
+    achieved_per_launch: the same bytes over the mean event-timed launch."""
+    step_s = float(step_ms) / 1e3
     launch_s = float(per_launch_ms.mean()) / 1e3
-    achieved = alg_bytes_per_launch / launch_s / 1e9
+    achieved = alg_bytes_per_launch / step_s / 1e9
+    per_launch = alg_bytes_per_launch / launch_s / 1e9
     return {
         "bound": "hbm",
         "achieved": round(achieved, 2),
@@ -228,6 +333,9 @@ def roofline(alg_bytes_per_launch, per_launch_ms, kernel, traffic):
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
         "kernel": kernel,
+        "step_us_median": round(step_s * 1e6, 2),
+        "achieved_per_launch": round(per_launch, 2),
+        "frac_per_launch": round(per_launch / HBM_PEAK_GBPS, 4),
         "launch_us_mean": round(launch_s * 1e6, 2),
         "launch_us_p50": round(float(np.median(per_launch_ms)) * 1e3, 2),
     }
@@ -294,9 +402,9 @@ def main():
     k, v, mask = W.initial_cache(wl)
     fill_from = None
     if args.mode == "fill":
-        # every sequence starts 2K + W slots short of full and fills up by the last step
-        # (W warm-up steps, K timed steps, K steps with per-launch events)
-        fill_from = max(1, wl.S - (2 * K + Wm))
+        # every timed pass starts from the same state, every sequence K slots short
+        # of full, and fills up at its last step (the mask is restored between passes)
+        fill_from = max(1, wl.S - K)
         mask = (np.arange(wl.S)[None, :] < fill_from).astype(np.uint8).repeat(wl.B, 0)
         W.poison_free(k, v, mask)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -342,32 +450,38 @@ def main():
             if (t + 1) % N == 0:
                 lf.longflow_evict_topk(scores, dm, N, out=queue, stream=stream)
 
-    ms_per_step, per_launch, wall = timed(step, K, Wm, stream, dev)
+    reset = None
+    if args.mode == "fill":
+        dm0 = dm.clone()
+
+        def reset(t):
+            dm.copy_(dm0)
+            slots[t % 2].fill_(fill_from if fill_from < wl.S else -1)
+
+    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev, reset)
+    ms_per_step = float(np.median(reps))
     status = lf.lf_read_device_status(ws)
     if status:
         raise RuntimeError(f"device status flags set during the run: {status:#x}")
 
     if args.mode == "fill":
-        def fill_bytes(t0):
-            # valid rows of step t (warm-up included): the prefix plus the t + 1 written slots
-            rows = sum(min(wl.S, fill_from + t + 1) for t in range(t0, t0 + K)) / K
-            kv = int(rows * wl.B * wl.Hkv * wl.d * 2 * 2)
-            return kv, kv + algorithmic_bytes(wl, np.zeros_like(mask)) + wl.B
-        kvb, algb = fill_bytes(Wm)               # the timed steps
-        _, algb_launch = fill_bytes(Wm + K)      # the steps with per-launch events
-        final_mask = dm.cpu().numpy()
-        if not final_mask.all() and fill_from + Wm + 2 * K >= wl.S:
-            raise RuntimeError("fill run ended with free slots left")
+        # valid rows of the t-th step of a pass: the prefix plus the t + 1 written slots
+        rows = sum(min(wl.S, fill_from + t + 1) for t in range(K)) / K
+        kvb = int(rows * wl.B * wl.Hkv * wl.d * 2 * 2)
+        algb = algb_launch = kvb + algorithmic_bytes(wl, np.zeros_like(mask)) + wl.B
+        if not dm.cpu().numpy().all():
+            raise RuntimeError("fill pass ended with free slots left")
     else:
         kvb = kv_bytes(wl, mask)
         algb = algb_launch = algorithmic_bytes(wl, mask)
-    # step index of the per-launch durations: Wm + K + t
+    # step index of the per-launch durations: warm + REPEATS * K + t
+    first_launch = warm + REPEATS * K
     if args.mode == "cadence":
         # decode launches only: top-k launches are timed inside the steps that run them
-        dec = np.array([x for t, x in enumerate(per_launch) if (Wm + K + t + 1) % N != 0])
-        rl = roofline(algb, dec if dec.size else per_launch, "longflow_decode_kernel", None)
+        dec = np.array([x for t, x in enumerate(per_launch) if (first_launch + t + 1) % N != 0])
+        rl = roofline(algb, ms_per_step, dec if dec.size else per_launch, "longflow_decode_kernel", None)
     else:
-        rl = roofline(algb_launch, per_launch, "longflow_decode_kernel",
+        rl = roofline(algb_launch, ms_per_step, per_launch, "longflow_decode_kernel",
                       measured_traffic(f"{wl.name}/nsplit{nsplit}" + ("/fill" if args.mode == "fill" else "")))
     metric = {
         "decode": METRIC,
@@ -398,13 +512,17 @@ def main():
         "pct_hbm_peak": round(100 * algb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
         "alg_bytes_per_step": algb,
         "roofline": rl,
+        "timing": {"repeats": REPEATS, "steps_per_repeat": K, "statistic": "median",
+                   "ms_per_step_repeats": [round(float(x), 5) for x in reps],
+                   "warmup_steps_run": warm, "warmup_min_s": WARMUP_MIN_S},
         "wall_s_timed": round(wall, 3),
     }
+    result["hbm_probe"] = hbm_probes(dev)
     if args.mode == "fill":
         result["config"].update({"mode": "fill", "start_valid_slots": fill_from})
     if args.mode == "cadence":
         result["config"].update({"mode": "cadence", "cadence": N})
-        refresh = [x for t, x in enumerate(per_launch) if (Wm + K + t + 1) % N == 0]
+        refresh = [x for t, x in enumerate(per_launch) if (first_launch + t + 1) % N == 0]
         if refresh:
             result["refresh_step_us_mean"] = round(float(np.mean(refresh)) * 1e3, 2)
     if not args.no_cpu_baseline and args.mode != "cadence":
@@ -430,7 +548,8 @@ def bench_topk(args, wl, lf, W, dev):
     def step(t):
         lf.longflow_evict_topk(scores, mask, k, out=out, stream=stream)
 
-    ms, per_launch, wall = timed(step, K, Wm, stream, dev)
+    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev)
+    ms = float(np.median(reps))
     algb = topk_bytes(B, Hkv, S, k)
     result = {
         "metric": f"k-slot eviction (k={k}): scores GB/s, launches/s at B={B}, {S} slots",
@@ -449,7 +568,9 @@ def bench_topk(args, wl, lf, W, dev):
                    "scores": "ties"},
         "steps_per_s": round(1e3 / ms, 2),
         "alg_bytes_per_step": algb,
-        "roofline": roofline(algb, per_launch, "evict_topk_kernel", measured_traffic(f"topk/{wl.name}/k{k}")),
+        "roofline": roofline(algb, ms, per_launch, "evict_topk_kernel", measured_traffic(f"topk/{wl.name}/k{k}")),
+        "timing": {"repeats": REPEATS, "steps_per_repeat": K, "statistic": "median",
+                   "ms_per_step_repeats": [round(float(x), 5) for x in reps], "warmup_steps_run": warm},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
@@ -531,7 +652,8 @@ def bench_stack(args, wl, lf, W, dev):
         x_in.copy_(xs[t % n_inputs], non_blocking=True)
         graph.launch(stream)
 
-    ms, per_launch, wall = timed(step, K, Wm, stream, dev)
+    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev)
+    ms = float(np.median(reps))
     status = lf.lf_read_device_status(stack.tensors["workspace"])
     graph.close()
     if status:
@@ -560,7 +682,9 @@ def bench_stack(args, wl, lf, W, dev):
         "steps_per_s": round(1e3 / ms, 2),
         "alg_bytes_per_step": algb,
         "weight_bytes_per_step": wb,
-        "roofline": roofline(algb, per_launch, f"{L}-layer step (graph)", None),
+        "roofline": roofline(algb, ms, per_launch, f"{L}-layer step (graph)", None),
+        "timing": {"repeats": REPEATS, "steps_per_repeat": K, "statistic": "median",
+                   "ms_per_step_repeats": [round(float(x), 5) for x in reps], "warmup_steps_run": warm},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -29,10 +29,19 @@ _FAMILIES = {"decode": ["longflow_kernels.hip"], "topk": ["evict_topk.hip"],
 _HEADERS = {"decode": ["longflow.h"], "topk": ["longflow.h"], "stack": ["longflow.h", "longflow_stack.h"]}
 
 
+# Code-generation flags; part of the whole library's source hash.
+CODEGEN_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # keep the compiler from forming packed fp32 vector ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+HASH_TAG = b"lf-source-hash:"
+
+
 def source_hash(family=None):
     """Short hash of the sources of one kernel family ("decode", "topk",
-    "stack"), or of the whole library when family is None; identifies a
-    kernel build."""
+    "stack"), or of the whole library (every source, header and the
+    code-generation flags) when family is None; identifies a build."""
     import hashlib
     if family is None:
         names = _COMMON + sorted({n for v in _FAMILIES.values() for n in v})
@@ -44,7 +53,23 @@ def source_hash(family=None):
     for path in sorted([os.path.join(CSRC, n) for n in names] + [os.path.join(INCLUDE, n) for n in headers]):
         with open(path, "rb") as f:
             h.update(f.read())
+    if family is None:
+        h.update(" ".join(CODEGEN_FLAGS).encode())
     return h.hexdigest()[:16]
+
+
+def built_hash(path=LIB_PATH):
+    """The source hash recorded in a built library (read from the file, not
+    loaded), or None."""
+    try:
+        with open(path, "rb") as f:
+            data = f.read()
+    except OSError:
+        return None
+    at = data.find(HASH_TAG)
+    if at < 0:
+        return None
+    return data[at + len(HASH_TAG):at + len(HASH_TAG) + 16].decode("ascii", "replace")
 
 
 def hipcc():
@@ -56,9 +81,7 @@ def hipcc():
 
 def compile_command(out_path):
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # keep the compiler from forming packed fp32 vector ops
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        hipcc(), *CODEGEN_FLAGS, f'-DLF_SOURCE_HASH="{source_hash()}"',
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", out_path,
     ]
@@ -82,8 +105,9 @@ def build(verbose=False):
 
 
 def ensure_built():
-    """Path of the built library, building it only if it is absent."""
-    if not os.path.exists(LIB_PATH):
+    """Path of the built library, building it when it is absent or was built
+    from other sources than the current ones."""
+    if built_hash() != source_hash():
         build()
     return LIB_PATH
 

@@ -15,26 +15,15 @@
 namespace lf {
 
 constexpr int kMaxGroup = 8;          // query heads per KV head supported
-// Tuning knobs of the decode kernel; the defaults are the shipped choice.
-#ifndef LF_WAVES_SMALL_LDS
-#define LF_WAVES_SMALL_LDS 8  // wavefronts per workgroup when two workgroups fit a CU's LDS
-#endif
-#ifndef LF_WAVES_LARGE_LDS
-#define LF_WAVES_LARGE_LDS 16  // wavefronts per workgroup when one workgroup fills the LDS
-#endif
-#ifndef LF_UNROLL
-#define LF_UNROLL 4  // 16-byte row loads per lane per batch
-#endif
+constexpr int kWavesSmallLds = 8;   // wavefronts per workgroup when two workgroups fit a CU's LDS
+constexpr int kWavesLargeLds = 16;  // wavefronts per workgroup when one workgroup fills the LDS
+constexpr int kUnroll = 4;          // 16-byte row loads per lane per batch
 // Occupancy hint given to the register allocator, by padded group size:
 // waves per SIMD the kernel must fit (512 VGPRs per lane / waves).
-#ifndef LF_WAVES_PER_EU_SMALL
-#define LF_WAVES_PER_EU_SMALL 5  // groups of up to 4 query heads
-#endif
-#ifndef LF_WAVES_PER_EU_LARGE
-#define LF_WAVES_PER_EU_LARGE 4  // groups of 8
-#endif
+constexpr int kWavesPerEuSmall = 5;  // groups of up to 4 query heads
+constexpr int kWavesPerEuLarge = 4;  // groups of 8
 
-constexpr int kMaxWaves = LF_WAVES_LARGE_LDS > LF_WAVES_SMALL_LDS ? LF_WAVES_LARGE_LDS : LF_WAVES_SMALL_LDS;
+constexpr int kMaxWaves = kWavesLargeLds > kWavesSmallLds ? kWavesLargeLds : kWavesSmallLds;
 constexpr int kMaxSplits = 1024;      // slot splits per (sequence, KV head)
 // Largest split count the team path takes: every split of a team reads the
 // (max, sum) words of all the others, so the exchange grows with the square
@@ -47,10 +36,7 @@ LF_HD inline int ticket_range_first_pair(int pairs, int r) {
   return (int)((long long)pairs * r / kTicketRanges);
 }
 // LDS bytes a workgroup may spend on the logits of its slot range.
-#ifndef LF_LOGIT_LDS_KB
-#define LF_LOGIT_LDS_KB 136
-#endif
-constexpr size_t kLogitLdsBudget = (size_t)LF_LOGIT_LDS_KB * 1024;
+constexpr size_t kLogitLdsBudget = (size_t)136 * 1024;
 
 LF_HD inline int padded_group(int g) {
   int p = 1;
@@ -169,8 +155,8 @@ constexpr size_t kHalfLdsBytes = 80 * 1024;
 // them (which reach their barriers independently) share the CU.
 LF_HD inline int decode_waves(int gp, int split_len) {
   return (size_t)(split_len + kRowPad) * gp * 4 + split_len + kRowPad + kScratchBytes > kHalfLdsBytes
-             ? LF_WAVES_LARGE_LDS
-             : LF_WAVES_SMALL_LDS;
+             ? kWavesLargeLds
+             : kWavesSmallLds;
 }
 
 LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len, int nw) {

@@ -14,7 +14,16 @@
 #include "longflow.h"
 
 
+#ifndef LF_SOURCE_HASH
+#define LF_SOURCE_HASH "unknown"
+#endif
+
 namespace {
+
+// The hash of the sources this library was built from, behind a tag that
+// the build script can find in the file without loading it.
+const char kSourceHashTag[] = "lf-source-hash:" LF_SOURCE_HASH;
+constexpr size_t kSourceHashTagLen = sizeof("lf-source-hash:") - 1;
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_num_cus[kMaxDevices];
@@ -33,6 +42,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 extern "C" {
 
 int lf_version(void) { return LF_ABI_VERSION; }
+
+const char* lf_source_hash(void) { return kSourceHashTag + kSourceHashTagLen; }
 
 const char* lf_strerror(int code) {
   switch (code) {
@@ -93,6 +104,12 @@ int lf_workspace_size(int B, int Hq, int Hkv, int d, int S, int nsplit, size_t* 
   if (!bytes) return LF_E_NULL;
   int rc = lf_check_shape(B, Hq, Hkv, d, S);
   if (rc != LF_OK) return rc;
+  if (nsplit == 0) {
+    // The count longflow_decode plans for the current device.
+    int cus = 0;
+    if ((rc = lf_device_num_cus(&cus)) != LF_OK) return rc;
+    if ((rc = lf_plan_nsplit(B, Hq, Hkv, d, S, cus, &nsplit)) != LF_OK) return rc;
+  }
   if (nsplit < 1 || nsplit > S || nsplit > lf::kMaxSplits) return LF_E_NSPLIT;
   int len, eff;
   lf::split_geometry(S, nsplit, &len, &eff);

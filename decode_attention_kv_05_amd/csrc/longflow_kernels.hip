@@ -67,37 +67,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Cache policy of the K/V stream: rows are read once per step, so they may
-// be marked non-temporal (nt) to leave the caches to everything else.
-#ifndef LF_NT_LOADS
-#define LF_NT_LOADS 1
-#endif
-#ifndef LF_STREAM_POLICY
-#define LF_STREAM_POLICY 2  // cache-policy bits of the buffer load: nt
-#endif
-constexpr int kStreamPolicy = LF_NT_LOADS ? LF_STREAM_POLICY : 0;
+// Cache policy of the K/V stream: rows are read once per step, so they are
+// marked non-temporal (nt, policy bit 1) to leave the caches to everything
+// else (about 6% faster than the default policy).
+constexpr int kStreamPolicy = 2;
 
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
   const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, kStreamPolicy);
   return make_uint4(x.x, x.y, x.z, x.w);
-}
-
-// Sum of the absolute values of the 8 bf16 in a 16-byte chunk, in fp32
-// (sign bits cleared, then dotted with (1, 1)).
-__device__ __forceinline__ float abs_sum8_bf16(const uint4& a) {
-  const uint32_t ones = 0x3f803f80u;  // bf16 (1.0, 1.0)
-  float s = 0.f;
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w & 0x7fff7fffu), __builtin_bit_cast(bf16x2_t, ones), s, false);
-  return s;
-}
-
-// bf16 pair (lo, hi) from two fp32 values, round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
 }
 
 // fp32 sum of the 8 products of two rows of 8 bf16 values, plus `acc`
@@ -205,61 +182,35 @@ constexpr uint64_t kNoCandidate = ~0ull;
 // Keeps the scheduler from hoisting the LDS reads and conversions of later
 // rows of a batch above the current one, which would multiply the live
 // registers per wave (and so cut the waves per CU that keep loads in flight).
-#ifndef LF_ROW_FENCE_ON
-#define LF_ROW_FENCE_ON 1
-#endif
-#if LF_ROW_FENCE_ON
 #define LF_ROW_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define LF_ROW_FENCE() ((void)0)
-#endif
 
 // Ties 8 accumulators to this point of the program (an empty asm that reads
 // and writes them), so the compiler cannot gather the FMAs of all rows of a
 // batch at its end and keep every row's converted values live meanwhile.
 __device__ __forceinline__ void pin8(float (&a)[8]) {
-#if LF_ROW_FENCE_ON
   asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
                "+v"(a[6]), "+v"(a[7]));
-#endif
 }
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kInf = __builtin_huge_valf();
 
 // ------------------------------------------------------------ decode kernel
 
-// Phase V accumulates e * v with v_dot2 over pairs of rows (one lane holds
-// the same 8 columns of rows u and u + 1 of a batch): the two rows' values
-// are interleaved into bf16 pairs with v_perm, the probabilities are rounded
-// to bf16 for the output only (scores keep fp32 probabilities), halving the
-// fp32 FMAs of the output accumulation.
-#ifndef LF_PV_DOT2
-#define LF_PV_DOT2 0
-#endif
 // Stagger of the streaming order in the split and team modes: each wave
-// starts at batch (workgroup index * LF_ROTATE) mod (its batch count);
-// 0 = in order.
+// starts at batch (workgroup index * kRotate) mod (its batch count).
 // Splits of a power-of-two number of rows otherwise stream in lockstep from
 // addresses a power of two apart (long_reasoning: 269.8 -> 248.6 us/step);
-// the single-split kernel measured no better staggered (ragged 3% slower).
-#ifndef LF_ROTATE
-#define LF_ROTATE 5
-#endif
-#ifndef LF_ROTATE_SINGLE
-#define LF_ROTATE_SINGLE 0  // also stagger the single-split kernel
-#endif
-// Issue the first V batch before the softmax-statistics barriers.
-#ifndef LF_PREFETCH_V
-#define LF_PREFETCH_V 0
-#endif
+// the single-split kernel measured no better staggered (ragged 3% slower),
+// so it streams in order.
+constexpr int kRotate = 5;
 
-constexpr int waves_per_eu(int gp) { return gp >= 8 ? LF_WAVES_PER_EU_LARGE : LF_WAVES_PER_EU_SMALL; }
+constexpr int waves_per_eu(int gp) { return gp >= 8 ? kWavesPerEuLarge : kWavesPerEuSmall; }
 
 template <int D, int GP>
 struct Shape {
   static constexpr int LPR = D / 8;                     // lanes per row (16 bytes each)
   static constexpr int RPW = 64 / LPR;                  // rows per wave load
-  static constexpr int U = LF_UNROLL;                   // wave loads per batch
+  static constexpr int U = kUnroll;                   // wave loads per batch
   static constexpr int ROWS = RPW * U;                  // rows per wave batch
   static constexpr int HPL = GP > LPR ? GP / LPR : 1;   // heads per lane after reduce-scatter
   static constexpr int LPH = GP < LPR ? LPR / GP : 1;   // lanes holding each head
@@ -458,7 +409,7 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   // that workgroups streaming at the same pace read addresses that differ
   // by more than the power-of-two spacing of their cache rows.
   const int nbatch = wave * ROWS < n_eff ? (n_eff - wave * ROWS + stride - 1) / stride : 0;
-  const int rot = LF_ROTATE && (MODE != kModeSingle || LF_ROTATE_SINGLE) && nbatch > 0 ? (int)(((unsigned)item * LF_ROTATE) % (unsigned)nbatch) : 0;
+  const int rot = MODE != kModeSingle && nbatch > 0 ? (int)(((unsigned)item * kRotate) % (unsigned)nbatch) : 0;
   for (int bi = 0; bi < nbatch; ++bi) {
     const int r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
     uint4 buf[U];
@@ -480,13 +431,6 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
       LF_ROW_FENCE();
     }
   }
-
-  // The first V batch goes out before the softmax barriers, so the stream
-  // keeps going while the statistics are formed.
-  uint4 vbuf[U];
-  uint32_t vok = 0;
-  if (LF_PREFETCH_V && nbatch > 0)
-    vok = load_batch<D, U, RPW>(vbuf, vrs, mk, wave * ROWS + rot * stride, rg, c);
 
   // ---- softmax statistics of this split
   // Lanes with equal c hold the same heads; fold the row groups, then waves.
@@ -606,65 +550,28 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   };
   for (int bi = 0; bi < nbatch; ++bi) {
     const int r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
-    if (!LF_PREFETCH_V || bi != 0)
-      vok = load_batch<D, U, RPW>(vbuf, vrs, mk, r0, rg, c);
+    uint4 vbuf[U];
+    const uint32_t vok = load_batch<D, U, RPW>(vbuf, vrs, mk, r0, rg, c);
     float* lrow = lg + (r0 + rg) * GP;
-    if constexpr (LF_PV_DOT2) {
-      static_assert(U % 2 == 0, "rows are paired");
 #pragma unroll
-      for (int u = 0; u < U; u += 2) {
-        const bool va = (vok >> u) & 1u, vb = (vok >> (u + 1)) & 1u;
-        float ea[GP], eb[GP];
-        uint32_t ep[GP];
+    for (int u = 0; u < U; ++u) {
+      const bool valid = (vok >> u) & 1u;
+      float vf[8];
+      bf16x8_to_f32(vbuf[u], vf);
+      float e[GP];  // exactly 0 for invalid rows (see the softmax pass)
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-          const float xa = lrow[u * RPW * GP + h];  // padded: in range even past the split
-          const float xb = lrow[(u + 1) * RPW * GP + h];
-          ea[h] = va ? xa : 0.f;
-          eb[h] = vb ? xb : 0.f;
-          ep[h] = pack_bf16x2(ea[h], eb[h]);
-        }
-        const uint4 a = vbuf[u], bq = vbuf[u + 1];
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {bq.x, bq.y, bq.z, bq.w};
-        uint32_t vp[8];
+      for (int h = 0; h < GP; ++h) e[h] = lrow[u * RPW * GP + h];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          vp[2 * w] = __builtin_amdgcn_perm(bw[w], aw[w], 0x05040100u);      // (a lo, b lo)
-          vp[2 * w + 1] = __builtin_amdgcn_perm(bw[w], aw[w], 0x07060302u);  // (a hi, b hi)
-        }
+      for (int h = 0; h < GP; ++h) {
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            acc[h][k] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ep[h]),
-                                                        __builtin_bit_cast(bf16x2_t, vp[k]), acc[h][k], false);
-          pin8(acc[h]);
-        }
-        finish_row(lrow + u * RPW * GP, abs_sum8_bf16(a), ea, va, r0 + u * RPW + rg);
-        finish_row(lrow + (u + 1) * RPW * GP, abs_sum8_bf16(bq), eb, vb, r0 + (u + 1) * RPW + rg);
-        LF_ROW_FENCE();
+        for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(e[h], vf[k], acc[h][k]);
+        pin8(acc[h]);
       }
-    } else {
+      float vn = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool valid = (vok >> u) & 1u;
-        float vf[8];
-        bf16x8_to_f32(vbuf[u], vf);
-        float e[GP];  // exactly 0 for invalid rows (see the softmax pass)
-#pragma unroll
-        for (int h = 0; h < GP; ++h) e[h] = lrow[u * RPW * GP + h];
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(e[h], vf[k], acc[h][k]);
-          pin8(acc[h]);
-        }
-        float vn = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) vn += fabsf(vf[k]);
-        finish_row(lrow + u * RPW * GP, vn, e, valid, r0 + u * RPW + rg);
-        LF_ROW_FENCE();
-      }
+      for (int k = 0; k < 8; ++k) vn += fabsf(vf[k]);
+      finish_row(lrow + u * RPW * GP, vn, e, valid, r0 + u * RPW + rg);
+      LF_ROW_FENCE();
     }
   }
   __syncthreads();
@@ -1073,21 +980,21 @@ hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, int team
 
 template <int D, int GP>
 hipError_t launch_dg(const DecodeParams& prm, int nw, int nblocks, size_t lds, int team_grid, hipStream_t stream) {
-  if (nw == LF_WAVES_LARGE_LDS) return launch_dgw<D, GP, LF_WAVES_LARGE_LDS>(prm, nblocks, lds, team_grid, stream);
-  if (nw == LF_WAVES_SMALL_LDS) return launch_dgw<D, GP, LF_WAVES_SMALL_LDS>(prm, nblocks, lds, team_grid, stream);
+  if (nw == kWavesLargeLds) return launch_dgw<D, GP, kWavesLargeLds>(prm, nblocks, lds, team_grid, stream);
+  if (nw == kWavesSmallLds) return launch_dgw<D, GP, kWavesSmallLds>(prm, nblocks, lds, team_grid, stream);
   return hipErrorInvalidValue;
 }
 
 template <int D, int GP>
 hipError_t team_occupancy_dg(int nw, size_t lds, int* blocks) {
-  if (nw == LF_WAVES_LARGE_LDS)
+  if (nw == kWavesLargeLds)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, LF_WAVES_LARGE_LDS, kModeTeam>),
-        LF_WAVES_LARGE_LDS * 64, lds);
-  if (nw == LF_WAVES_SMALL_LDS)
+        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, kWavesLargeLds, kModeTeam>),
+        kWavesLargeLds * 64, lds);
+  if (nw == kWavesSmallLds)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, LF_WAVES_SMALL_LDS, kModeTeam>),
-        LF_WAVES_SMALL_LDS * 64, lds);
+        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, kWavesSmallLds, kModeTeam>),
+        kWavesSmallLds * 64, lds);
   return hipErrorInvalidValue;
 }
 

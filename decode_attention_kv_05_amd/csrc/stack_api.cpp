@@ -196,6 +196,22 @@ int lf_stack_workspace_size(int L, int B, int H, int Hq, int Hkv, int d, int S, 
   return LF_OK;
 }
 
+int lf_stack_workspace_offsets(int B, int H, int Hq, int Hkv, int d, int S, int nsplit,
+                               size_t* offsets) {
+  if (!offsets) return LF_E_NULL;
+  int rc = check_stack_shape(1, B, H, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  size_t dec = 0;
+  rc = lf_workspace_size(B, Hq, Hkv, d, S, nsplit < 1 ? -1 : nsplit, &dec);
+  if (rc != LF_OK) return rc;
+  const StackLayout w = stack_layout(B, H, Hq, Hkv, d, S, dec);
+  offsets[0] = w.q;
+  offsets[1] = w.k;
+  offsets[2] = w.v;
+  offsets[3] = w.o;
+  return LF_OK;
+}
+
 int longflow_stack_step(int L, int B, int H, int Hq, int Hkv, int d, int S, float scale,
                         float rope_base, const void* x_in, void* x_out, int32_t* pos,
                         int advance_pos, const void* const* w_qkv, const void* const* w_o,

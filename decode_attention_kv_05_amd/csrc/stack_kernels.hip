@@ -248,9 +248,7 @@ __global__ void advance_pos_kernel(int32_t* pos, int n) {
 
 // Workgroups the K slices aim for (a 256-CU device); more slices keep more
 // compute units streaming weights but add fp32 partials to write and read.
-#ifndef LF_GEMM_TARGET_WG
-#define LF_GEMM_TARGET_WG 256
-#endif
+constexpr int kGemmTargetWorkgroups = 256;
 
 int gemm_ksplit(int N, int K) {
   const int blocks = (N + kGemmCols - 1) / kGemmCols;
@@ -259,7 +257,7 @@ int gemm_ksplit(int N, int K) {
   int ks = 1;
   while (pieces / ks > 8 || pieces % ks != 0) ++ks;
   // ... then more slices while the grid stays within the workgroup target
-  for (int c = ks + 1; c <= pieces && blocks * c <= LF_GEMM_TARGET_WG; ++c)
+  for (int c = ks + 1; c <= pieces && blocks * c <= kGemmTargetWorkgroups; ++c)
     if (pieces % c == 0) ks = c;
   return ks;
 }

@@ -11,7 +11,7 @@ import os
 
 import torch
 
-from .build import LIB_PATH
+from .build import LIB_PATH, source_hash
 
 LF_OK = 0
 LF_E_NULL = -1
@@ -32,11 +32,11 @@ LF_SPLIT_AUTO, LF_SPLIT_COMBINE, LF_SPLIT_TEAM = 0, 1, 2
 SPLIT_PATHS = {"auto": LF_SPLIT_AUTO, "combine": LF_SPLIT_COMBINE, "team": LF_SPLIT_TEAM}
 
 EXPORTED = (
-    "lf_version", "lf_strerror", "lf_check_shape", "lf_plan_nsplit", "lf_workspace_size",
+    "lf_version", "lf_source_hash", "lf_strerror", "lf_check_shape", "lf_plan_nsplit", "lf_workspace_size",
     "lf_device_num_cus", "lf_workspace_init", "lf_validate", "longflow_decode",
     "longflow_decode_nsplit", "longflow_decode_fill", "longflow_decode_ex", "longflow_evict_topk",
     "lf_read_device_status",
-    "lf_stack_workspace_size", "longflow_stack_step", "lf_stack_graph_create", "lf_graph_launch",
+    "lf_stack_workspace_size", "lf_stack_workspace_offsets", "longflow_stack_step", "lf_stack_graph_create", "lf_graph_launch",
     "lf_graph_destroy",
 )
 
@@ -49,6 +49,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
         "lf_version": ([], _i),
+        "lf_source_hash": ([], ctypes.c_char_p),
         "lf_strerror": ([_i], ctypes.c_char_p),
         "lf_check_shape": ([_i] * 5, _i),
         "lf_plan_nsplit": ([_i] * 6 + [ctypes.POINTER(_i)], _i),
@@ -63,6 +64,7 @@ def _load():
         "longflow_evict_topk": ([_i] * 4 + [_p] * 3 + [_p], _i),
         "lf_read_device_status": ([_p, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
         "lf_stack_workspace_size": ([_i] * 8 + [ctypes.POINTER(_sz)], _i),
+        "lf_stack_workspace_offsets": ([_i] * 7 + [ctypes.POINTER(_sz)], _i),
         "longflow_stack_step": ([_i] * 7 + [_f, _f] + [_p] * 3 + [_i] + [_p] * 8 + [_sz, _i, _p], _i),
         "lf_stack_graph_create": ([_i] * 7 + [_f, _f] + [_p] * 3 + [_i] + [_p] * 8 + [_sz, _i,
                                                                              ctypes.POINTER(_p)], _i),
@@ -73,6 +75,10 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    built, want = lib.lf_source_hash().decode(), source_hash()
+    if built != want:
+        raise ImportError(f"{LIB_PATH} was built from other sources ({built}) than the current ones ({want}): "
+                          "run `python -m decode_attention_kv_05_amd.build`")
     return lib
 
 
@@ -94,6 +100,10 @@ def _check(rc, where):
 
 def lf_version():
     return _lib.lf_version()
+
+
+def lf_source_hash():
+    return _lib.lf_source_hash().decode()
 
 
 def lf_strerror(code):
@@ -166,8 +176,19 @@ def _need(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+class DeviceStatusError(RuntimeError):
+    """LF_DEV_* bits found in a workspace after a step (see check=True)."""
+
+    def __init__(self, flags):
+        self.flags = flags
+        names = [n for n, bit in (("LF_DEV_BAD_PREV", LF_DEV_BAD_PREV), ("LF_DEV_WRITE_MASKED", LF_DEV_WRITE_MASKED),
+                                  ("LF_DEV_FILL_DIVERGED", LF_DEV_FILL_DIVERGED),
+                                  ("LF_DEV_TEAM_TIMEOUT", LF_DEV_TEAM_TIMEOUT)) if flags & bit]
+        super().__init__(f"device status {flags:#x}: {', '.join(names) or 'unknown bits'}")
+
+
 def _step(entry, q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out, scores, evict_slot,
-          workspace, nsplit, stream, split_path=None):
+          workspace, nsplit, stream, split_path=None, check=False):
     B, Hq, d = q.shape
     Hkv, S = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
@@ -212,12 +233,16 @@ def _step(entry, q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
             ptr(evict_slot), ptr(workspace), workspace.numel() * workspace.element_size(), int(nsplit),
             SPLIT_PATHS[split_path], _stream_ptr(stream, dev))
     _check(rc, entry)
+    if check:
+        flags = lf_read_device_status(workspace, stream)
+        if flags:
+            raise DeviceStatusError(flags)
     return out, scores, evict_slot
 
 
 def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
                     out=None, scores=None, evict_slot=None, workspace=None, nsplit=None,
-                    stream=None, split_path=None):
+                    stream=None, split_path=None, check=False):
     """One fused decode step; returns (out, scores, evict_slot).
 
     q [B, Hq, d] bf16; k_cache, v_cache [B, Hkv, S, d] bf16 (updated in place);
@@ -228,15 +253,18 @@ def longflow_decode(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale
     device.  The work is enqueued on `stream` (default: torch's current
     stream) and not waited for.  split_path ("auto", "combine", "team"; None
     = "auto") chooses how a step with several splits is finished
-    (longflow_decode_ex).
+    (longflow_decode_ex).  check=True waits for the step and raises
+    DeviceStatusError if the workspace holds any LF_DEV_* bit, among them
+    LF_DEV_TEAM_TIMEOUT (a team-path step whose results are unspecified
+    because another process kept some of its workgroups from running).
     """
     return _step("longflow_decode_nsplit", q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
-                 scores, evict_slot, workspace, nsplit, stream, split_path)
+                 scores, evict_slot, workspace, nsplit, stream, split_path, check)
 
 
 def longflow_decode_fill(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, scale=None,
                          out=None, scores=None, next_slot=None, workspace=None, nsplit=None,
-                         stream=None, split_path=None):
+                         stream=None, split_path=None, check=False):
     """One decode step of the fill phase; returns (out, scores, next_slot).
 
     As longflow_decode, except that `mask` is updated in place (the written
@@ -244,7 +272,7 @@ def longflow_decode_fill(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, 
     mask while the sequence has one, else the evicted slot.
     """
     return _step("longflow_decode_fill", q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
-                 scores, next_slot, workspace, nsplit, stream, split_path)
+                 scores, next_slot, workspace, nsplit, stream, split_path, check)
 
 
 def longflow_evict_topk(scores, mask, k, *, out=None, stream=None):
@@ -278,6 +306,13 @@ def lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, nsplit):
     _check(_lib.lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, nsplit, ctypes.byref(out)),
            "lf_stack_workspace_size")
     return out.value
+
+
+def lf_stack_workspace_offsets(B, H, Hq, Hkv, d, S, nsplit):
+    """Byte offsets of the last layer's q, k_new, v_new and O in a stack workspace."""
+    out = (_sz * 4)()
+    _check(_lib.lf_stack_workspace_offsets(B, H, Hq, Hkv, d, S, nsplit, out), "lf_stack_workspace_offsets")
+    return tuple(out)
 
 
 class Stack:
@@ -341,6 +376,17 @@ class Stack:
     def step(self, stream=None):
         _check(_lib.longflow_stack_step(*self._args(), _stream_ptr(stream, self.tensors["x_in"].device)),
                "longflow_stack_step")
+
+    def intermediates(self):
+        """Views into the workspace of the last layer's q [B, Hq, d], k_new and
+        v_new [B, Hkv, d] and O [B, Hq d] (bf16), valid after a step until the
+        next one."""
+        L, B, H, Hq, Hkv, d, S = self.dims
+        offs = lf_stack_workspace_offsets(B, H, Hq, Hkv, d, S, self.nsplit)
+        ws = self.tensors["workspace"]
+        view = lambda off, shape: ws[off:off + 2 * int(torch.tensor(shape).prod())].view(torch.bfloat16).view(shape)
+        return {"q": view(offs[0], (B, Hq, d)), "k_new": view(offs[1], (B, Hkv, d)),
+                "v_new": view(offs[2], (B, Hkv, d)), "o": view(offs[3], (B, Hq * d))}
 
     def graph(self):
         return StackGraph(self)

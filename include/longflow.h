@@ -117,6 +117,10 @@ typedef enum lf_status {
 /* ABI version (LF_ABI_VERSION). */
 int lf_version(void);
 
+/* Hash of the source files the library was built from (16 hex digits, or
+ * "unknown" for a build that did not record it); never NULL. */
+const char* lf_source_hash(void);
+
 /* Static description of an lf_status code; never NULL. */
 const char* lf_strerror(int code);
 
@@ -131,7 +135,11 @@ int lf_check_shape(int B, int Hq, int Hkv, int d, int S);
  * path) or by a combine kernel (see longflow_decode_ex). */
 int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nsplit);
 
-/* Host-only workspace size in bytes for an explicit split count (>= 1). */
+/* Workspace size in bytes for a step with `nsplit` slot splits (>= 1), or,
+ * with nsplit = 0, for the count lf_plan_nsplit chooses for the current
+ * device: the size longflow_decode needs.  Host-only for nsplit >= 1; with
+ * nsplit = 0 it reads the current device's compute-unit count (LF_E_HIP
+ * when no device is usable). */
 int lf_workspace_size(int B, int Hq, int Hkv, int d, int S, int nsplit, size_t* bytes);
 
 /* Compute units of the current HIP device (cached per device). */
@@ -154,7 +162,7 @@ int lf_validate(int B, int Hq, int Hkv, int d, int S, float scale,
 /* One fused decode step (Figure 2, Left panel: write the previous choice,
  * attend, score, choose the next slot), with the split count chosen by
  * lf_plan_nsplit for the current device.  The workspace must hold at least
- * lf_workspace_size(..., nsplit, ...) bytes for that count. */
+ * lf_workspace_size(..., 0, &bytes) bytes (the size for that count). */
 int longflow_decode(int B, int Hq, int Hkv, int d, int S, float scale,
                     const void* q, void* k_cache, void* v_cache,
                     const uint8_t* mask, const void* new_k, const void* new_v,

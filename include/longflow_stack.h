@@ -64,6 +64,19 @@ extern "C" {
 int lf_stack_workspace_size(int L, int B, int H, int Hq, int Hkv, int d, int S, int nsplit,
                             size_t* bytes);
 
+/* Where a step leaves the intermediates of its last layer inside the
+ * workspace (sized by lf_stack_workspace_size for the same sizes and split
+ * count; nsplit >= 1): byte offsets from the workspace start of
+ *   offsets[0]  q after RoPE          bf16 [B][Hq][d]
+ *   offsets[1]  k_new after RoPE      bf16 [B][Hkv][d]
+ *   offsets[2]  v_new                 bf16 [B][Hkv][d]
+ *   offsets[3]  O, the operator's output, laid end to end  bf16 [B][Hq d]
+ * They hold the last layer's values from the end of a step until the next
+ * step on that workspace, so a step of one layer (L = 1) exposes every stage
+ * of that layer for inspection.  Host-only. */
+int lf_stack_workspace_offsets(int B, int H, int Hq, int Hkv, int d, int S, int nsplit,
+                               size_t* offsets);
+
 /* One decode step through all L layers, enqueued on `stream`. */
 int longflow_stack_step(int L, int B, int H, int Hq, int Hkv, int d, int S, float scale,
                         float rope_base, const void* x_in, void* x_out, int32_t* pos,

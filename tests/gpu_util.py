@@ -2,14 +2,16 @@
 acceptance rule against the oracle, and a lockstep driver that runs the HIP
 operator and the oracle on the same seeded inputs step after step."""
 
+import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
 
 from decode_attention_kv_05_amd import workloads as W
-from oracle import decode_step, decode_step_fill
+from oracle import decode_step, decode_step_fill, write_slot
 
 # Acceptance against the fp64 oracle (bf16 inputs, fp32 accumulation):
 O_ATOL = 1e-2
@@ -76,10 +78,51 @@ def compare_pair(o_gpu, s_gpu, e_gpu, o_ref, s_ref, e_ref, valid, where):
     return int(e_gpu) == int(e_ref)
 
 
+def oracle_workers():
+    """Host threads for the oracle: the process's CPU share, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_every_pair(q, k, v, mask, nk, nv, prev, scale):
+    """decode_step over every (sequence, KV head), one sequence per task on a
+    thread pool (numpy releases the GIL in the array work); the caches are
+    written in place as by one decode_step call over the whole batch."""
+    from threadpoolctl import threadpool_limits
+    B = q.shape[0]
+
+    def one(b):
+        return decode_step(q[b:b + 1], k[b:b + 1], v[b:b + 1], mask[b:b + 1], nk[b:b + 1], nv[b:b + 1],
+                           prev[b:b + 1], scale)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(oracle_workers()) as ex:
+        res = list(ex.map(one, range(B)))
+    return (np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res]),
+            np.concatenate([r[2] for r in res]))
+
+
+def fill_sentinels(out, scores, evict):
+    """Outputs a step must overwrite: NaN O and scores, -2 slots, so that a
+    pair the step leaves unwritten fails every later check."""
+    out.view(torch.int16).fill_(0x7FC0)
+    scores.fill_(float("nan"))
+    evict.fill_(-2)
+
+
+def all_outputs_written(out, sc, ev):
+    """No sentinel left: O finite everywhere, no NaN score, no -2 slot
+    (the workloads hold finite inputs only)."""
+    assert bool(torch.isfinite(out.float()).all()), "O not written (or not finite) for some pair"
+    assert not bool(torch.isnan(sc).any()), "scores not written for some pair"
+    assert bool((ev >= -1).all()), "evicted slot not written for some pair"
+
+
 class Lockstep:
     """Runs `steps` decode steps of workload `wl` on the GPU and, for the pairs
     in `pairs` (None = all), on the oracle; both sides continue from the GPU's
-    accepted eviction."""
+    accepted eviction.  The oracle's cache takes every pair's write each step,
+    so a step can be checked over every pair (step(all_pairs=True)) and the
+    whole cache compared at the end.  Outputs are preset to sentinels before
+    each step."""
 
     def __init__(self, wl, pairs=None, nsplit=None, device="cuda", state=None, split_path=None):
         from decode_attention_kv_05_amd import longflow as lf
@@ -103,32 +146,50 @@ class Lockstep:
         self.prev = W.first_prev_slot(wl)
         self.dprev = torch.from_numpy(self.prev).to(device)
         self.ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, nsplit, device)
+        self.out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=device)
+        self.sc = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device=device)
+        self.evs = [torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=device) for _ in range(2)]
         self.t = 0
         self.exact = 0
         self.total = 0
 
     def gpu_step(self, t):
         q, nk, nv = W.step_inputs(self.wl, t)
+        ev = self.evs[t % 2]
+        fill_sentinels(self.out, self.sc, ev)
         out, sc, ev = self.lf.longflow_decode(
             bf16_dev(q, self.device), self.dk, self.dv, self.dm, bf16_dev(nk, self.device),
-            bf16_dev(nv, self.device), self.dprev, scale=float(self.wl.scale), workspace=self.ws,
-            nsplit=self.nsplit, split_path=self.split_path)
+            bf16_dev(nv, self.device), self.dprev, scale=float(self.wl.scale), out=self.out, scores=self.sc,
+            evict_slot=ev, workspace=self.ws, nsplit=self.nsplit, split_path=self.split_path)
         torch.cuda.synchronize()
         return (q, nk, nv), out, sc, ev
 
-    def step(self, check=True, check_cache=True):
+    def step(self, check=True, check_cache=True, all_pairs=False):
+        """One lockstep step.  check: compare the sampled pairs (all_pairs:
+        every pair) with the oracle; every pair's cache write is applied to
+        the oracle's copy either way."""
         wl, t = self.wl, self.t
         (q, nk, nv), out, sc, ev = self.gpu_step(t)
         o_gpu = bf16_value(bf16_host(out))
         e_gpu = ev.cpu().numpy()
+        pairs = [(b, j) for b in range(wl.B) for j in range(wl.Hkv)] if all_pairs else self.pairs
+        checked = set(pairs) if check else set()
+        # the writes of the pairs the oracle does not run this step
+        for b in range(wl.B):
+            for j in range(wl.Hkv):
+                if (b, j) not in checked:
+                    write_slot(self.k_ref[b, j], self.v_ref[b, j], nk[b, j], nv[b, j], self.prev[b, j])
         if check:
-            bs = sorted({b for b, _ in self.pairs})
-            s_gpu = {}
-            for b in bs:
-                s_gpu[b] = sc[b].cpu().numpy().astype(np.float64)
-            o_ref, s_ref, e_ref = decode_step(q, self.k_ref, self.v_ref, self.mask, nk, nv, self.prev,
-                                              wl.scale, pairs=self.pairs)
-            for b, j in self.pairs:
+            if all_pairs:
+                o_ref, s_ref, e_ref = oracle_every_pair(q, self.k_ref, self.v_ref, self.mask, nk, nv, self.prev,
+                                                        wl.scale)
+                s_all = sc.cpu().numpy().astype(np.float64)
+                s_gpu = {b: s_all[b] for b in range(wl.B)}
+            else:
+                s_gpu = {b: sc[b].cpu().numpy().astype(np.float64) for b in sorted({b for b, _ in pairs})}
+                o_ref, s_ref, e_ref = decode_step(q, self.k_ref, self.v_ref, self.mask, nk, nv, self.prev,
+                                                  wl.scale, pairs=pairs)
+            for b, j in pairs:
                 heads = slice(j * wl.G, (j + 1) * wl.G)
                 valid = self.mask[b] != 0
                 self.exact += compare_pair(o_gpu[b, heads], s_gpu[b][j], e_gpu[b, j], o_ref[b, heads],
@@ -147,16 +208,14 @@ class Lockstep:
         return out, sc, ev
 
     def check_full_cache(self):
-        """The GPU cache equals the oracle's cache bitwise for the checked
-        sequences, and no step set a device status bit (bad or masked
-        prev_slot, diverged fill, team wait out of budget)."""
+        """The GPU cache equals the oracle's cache bitwise for every pair
+        (every step's write landed in its slot and nothing else changed), and
+        no step set a device status bit (bad or masked prev_slot, diverged
+        fill, team wait out of budget)."""
         assert self.lf.lf_read_device_status(self.ws) == 0
-        for b in sorted({b for b, _ in self.pairs}):
-            for j in range(self.wl.Hkv):
-                if (b, j) not in self.pairs:
-                    continue
-                assert np.array_equal(bf16_host(self.dk[b, j]), self.k_ref[b, j])
-                assert np.array_equal(bf16_host(self.dv[b, j]), self.v_ref[b, j])
+        for b in range(self.wl.B):
+            assert np.array_equal(bf16_host(self.dk[b]), self.k_ref[b]), f"K cache of sequence {b}"
+            assert np.array_equal(bf16_host(self.dv[b]), self.v_ref[b]), f"V cache of sequence {b}"
 
 
 def global_properties(sc, ev, dm):

@@ -6,6 +6,8 @@ test, so planted mistakes can be run through the same pins.
   RoPE                pos 0 is the identity; every pair keeps its norm;
                       rotations compose (a then b = a + b); a 2-dim head at
                       position p turns (1, 0) into (cos p, sin p) (math.cos);
+                      pairs i > 0 turn at hand-derived rates (d 4, base 100:
+                      pair 1 by p / 10; d 8, base 10^4: pair i by p / 10^i);
                       <R(m) q, R(n) k> depends only on m - n
   projection          identity and one-hot weights select inputs exactly
   residual            W_o = 0 leaves x unchanged
@@ -42,6 +44,22 @@ def pin_rope(rope, seed=52):
     p = 3.25
     r = rope(np.array([1.0, 0.0]), p, 10.0)
     assert abs(r[0] - math.cos(p)) < 1e-15 and abs(r[1] - math.sin(p)) < 1e-15
+    # Pairs beyond the first, at angles derived by hand: with d = 4 and base
+    # 100 the two pairs turn at 100^0 = 1 and 100^(-2/4) = 1/10 radian per
+    # position; with d = 8 and base 10^4, pair i turns at (10^4)^(-2i/8) =
+    # 10^-i.  Pair i couples coordinates i and i + d/2.
+    for p in (1.0, 7.0, 31.25):
+        r = rope(np.array([0.0, 1.0, 0.0, 0.0]), p, 100.0)
+        assert abs(r[1] - math.cos(p / 10)) < 1e-15 and abs(r[3] - math.sin(p / 10)) < 1e-15
+        assert r[0] == 0.0 and r[2] == 0.0
+        r = rope(np.array([1.0, 0.0, 0.0, 0.0]), p, 100.0)
+        assert abs(r[0] - math.cos(p)) < 1e-15 and abs(r[2] - math.sin(p)) < 1e-15
+        for i in range(4):
+            x8 = np.zeros(8)
+            x8[i] = 1.0
+            r = rope(x8, p, 1e4)
+            assert abs(r[i] - math.cos(p / 10 ** i)) < 1e-15 and abs(r[i + 4] - math.sin(p / 10 ** i)) < 1e-15
+            assert np.count_nonzero(r) <= 2
     q, k = rng.standard_normal(64), rng.standard_normal(64)
     for m, n in ((100, 40), (1060, 1000), (60, 0)):
         assert abs(np.dot(rope(q, m, 1e6), rope(k, n, 1e6)) - np.dot(rope(q, m - n, 1e6), k)) < 1e-9

@@ -395,3 +395,44 @@ def test_workspace_regions_fit_and_do_not_overlap(tmp_path):
     subprocess.run([gxx, "-std=c++17", "-O1", "-I", csrc, str(src), "-o", str(exe)], check=True)
     cases, bad = map(int, subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split())
     assert cases > 1000 and bad == 0, (cases, bad)
+
+
+def test_stack_workspace_offsets():
+    """The last layer's q, k_new, v_new and O sit in the stack workspace's
+    activation regions: after the decode workspace, 256-byte aligned,
+    disjoint and inside the size lf_stack_workspace_size reports."""
+    for B, H, Hq, Hkv, d, S, ns in ((3, 256, 8, 2, 64, 300, 1), (128, 4096, 32, 8, 128, 3200, 1),
+                                    (7, 2304, 18, 3, 128, 40, 3)):
+        offs = lf.lf_stack_workspace_offsets(B, H, Hq, Hkv, d, S, ns)
+        sizes = (B * Hq * d * 2, B * Hkv * d * 2, B * Hkv * d * 2, B * Hq * d * 2)
+        total = lf.lf_stack_workspace_size(1, B, H, Hq, Hkv, d, S, ns)
+        dec = lf.lf_workspace_size(B, Hq, Hkv, d, S, ns)
+        spans = sorted(zip(offs, sizes))
+        assert spans[0][0] >= dec and all(o % 256 == 0 for o in offs)
+        for (o1, n1), (o2, _) in zip(spans, spans[1:]):
+            assert o1 + n1 <= o2
+        assert spans[-1][0] + spans[-1][1] <= total
+    with pytest.raises(ValueError):
+        lf.lf_stack_workspace_offsets(3, 256, 8, 2, 64, 300, 0)
+
+
+def test_workspace_size_for_the_device_plan_needs_a_device():
+    """nsplit = 0 sizes the workspace for the device's own plan; with no
+    usable device the call reports LF_E_HIP (and an explicit count never
+    touches the device)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present; the GPU tests cover nsplit = 0")
+    out = ctypes.c_size_t(0)
+    rc = lf._lib.lf_workspace_size(128, 32, 8, 128, 3200, 0, ctypes.byref(out))
+    assert rc == lf.LF_E_HIP
+    assert lf.lf_workspace_size(128, 32, 8, 128, 3200, 1) == 256
+
+
+def test_library_records_its_source_hash():
+    """The built library carries the hash of the sources it was built from,
+    both as an export and as a tag in the file that the build script reads
+    without loading it; ensure_built rebuilds when they differ."""
+    from decode_attention_kv_05_amd.build import built_hash, source_hash
+    assert lf.lf_source_hash() == source_hash() == built_hash()
+    assert len(lf.lf_source_hash()) == 16

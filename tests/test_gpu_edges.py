@@ -36,14 +36,24 @@ def _largest_single_split(lf, G, d):
     return lo
 
 
-def test_auto_entry_point_matches_explicit_plan():
+@pytest.mark.parametrize("shape", [(3, 16, 4, 1500), (2, 64, 8, 16384), (16, 32, 8, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_auto_entry_point_matches_explicit_plan(shape):
+    """longflow_decode with the workspace sized by lf_workspace_size(...,
+    nsplit = 0, ...) equals longflow_decode_nsplit with the device plan's
+    count, bit for bit, and the long shape's step matches the oracle."""
     from decode_attention_kv_05_amd import longflow as lf
-    wl = W.Workload("auto", B=3, Hq=16, Hkv=4, d=128, S=1500, steps=1, kind="ragged", seed=9100, len_lo=100)
+    B, Hq, Hkv, S = shape
+    wl = W.Workload("auto", B=B, Hq=Hq, Hkv=Hkv, d=128, S=S, steps=1, kind="ragged", seed=9100, len_lo=100)
     k, v, mask = W.initial_cache(wl)
     q, nk, nv = W.step_inputs(wl, 0)
     assert lf.lf_device_num_cus() > 0
     ns = lf.plan_nsplit(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S)
-    ws_bytes = lf.lf_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, ns)
+    out_sz = ctypes.c_size_t(0)
+    assert lf._lib.lf_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, 0, ctypes.byref(out_sz)) == 0
+    ws_bytes = out_sz.value
+    assert ws_bytes == lf.lf_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, ns)
+    log(f"shape {shape}: plan {ns} splits, workspace {ws_bytes} bytes")
     results = []
     for use_auto in (True, False):
         dk, dv = bf16_dev(k), bf16_dev(v)
@@ -67,6 +77,14 @@ def test_auto_entry_point_matches_explicit_plan():
         results.append((bf16_host(out), sc.cpu().numpy(), ev.cpu().numpy(), bf16_host(dk)))
     for a, b in zip(*results):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    pairs = sorted({(0, 0), (wl.B - 1, wl.Hkv - 1)})
+    prev = np.full((wl.B, wl.Hkv), 3, dtype=np.int32)
+    o_ref, s_ref, e_ref = decode_step(q, k, v, mask, nk, nv, prev, wl.scale, pairs=pairs)
+    o = bf16_value(results[0][0])
+    for b, j in pairs:
+        heads = slice(j * wl.G, (j + 1) * wl.G)
+        compare_pair(o[b, heads], results[0][1][b, j].astype(np.float64), results[0][2][b, j], o_ref[b, heads],
+                     s_ref[b, j], e_ref[b, j], mask[b] != 0, f"auto {shape} b={b} j={j}")
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8])

@@ -1,16 +1,20 @@
 """The five named workloads at full size, in the launch configuration the
 benchmark times (the library's own split plan), for every decode step.
 
-The oracle checks a sample of (sequence, KV head) pairs in lockstep; every
-pair of every step is checked for the properties that hold at any size
-(masked scores +inf, the evicted slot is valid, holds the minimum score and
-is the lowest index among exact ties)."""
+The oracle checks every (sequence, KV head) pair of the first and of the
+last step, and a sample of pairs (the extremes of the batch, the shortest
+and longest ragged sequences) in every step between, in lockstep: both sides
+continue from the GPU's accepted slot.  Outputs are preset to sentinels
+before each step, and every pair of every step is checked for being written
+and for the properties that hold at any size (masked scores +inf, the
+evicted slot is valid, holds the minimum score and is the lowest index among
+exact ties).  At the end the whole cache equals the oracle's bit for bit."""
 
 import pytest
 import torch
 
 from decode_attention_kv_05_amd import workloads as W
-from gpu_util import Lockstep, Timer, global_properties, log
+from gpu_util import Lockstep, Timer, all_outputs_written, global_properties, log, oracle_workers
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -38,13 +42,17 @@ def test_full_workload(name):
     log(f"{name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} d={wl.d} S={wl.S} steps={wl.steps} pairs={pairs}")
     with Timer("generate + upload"):
         ls = Lockstep(wl, pairs=pairs)
-    with Timer(f"{wl.steps} lockstep steps"):
+    with Timer(f"{wl.steps} lockstep steps (every pair at steps 0 and {wl.steps - 1}, "
+               f"{oracle_workers()} oracle threads)"):
         for t in range(wl.steps):
-            out, sc, ev = ls.step()
+            every = t in (0, wl.steps - 1)
+            out, sc, ev = ls.step(all_pairs=every)
+            all_outputs_written(out, sc, ev)
             global_properties(sc, ev, ls.dm)
-            if t % 64 == 0:
-                log(f"  step {t} ok")
-    ls.check_full_cache()
+            if every or t % 64 == 0:
+                log(f"  step {t} ok ({'every pair' if every else f'{len(pairs)} pairs'} against the oracle)")
+    with Timer("whole cache against the oracle's"):
+        ls.check_full_cache()
     log(f"  evictions exactly equal to the oracle's: {ls.exact}/{ls.total}")
 
 
@@ -57,6 +65,7 @@ def test_full_long_reasoning_combine_path():
     log(f"long_reasoning, combine path, {wl.steps} steps, pairs={pairs}")
     ls = Lockstep(wl, pairs=pairs, nsplit=4, split_path="combine")
     for t in range(wl.steps):
-        out, sc, ev = ls.step()
+        out, sc, ev = ls.step(all_pairs=t == wl.steps - 1)
+        all_outputs_written(out, sc, ev)
         global_properties(sc, ev, ls.dm)
     ls.check_full_cache()

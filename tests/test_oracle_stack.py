@@ -54,6 +54,13 @@ def _rope_freq(x, pos, base):
     return np.concatenate([a * np.cos(ang) - b * np.sin(ang), b * np.cos(ang) + a * np.sin(ang)], axis=-1)
 
 
+def test_rope_frequency_mutant_fails_the_rope_pin_alone():
+    """The frequency schedule is pinned by pin_rope on its own (hand-derived
+    angles of pairs i > 0), not only through the assembled layer."""
+    with pytest.raises(AssertionError):
+        PS.pin_rope(_rope_freq)
+
+
 @pytest.mark.parametrize("mutant", [_rope_interleaved, _rope_sign, _rope_freq], ids=lambda f: f.__name__)
 def test_rope_mutants_caught(mutant, monkeypatch):
     """Wrong pair layout, wrong direction or wrong frequencies break a RoPE
