@@ -19,6 +19,7 @@ struct DecodeParams {
   float* scores;          // [B][Hkv][S]
   int32_t* evict;         // [B][Hkv]
   uint32_t* status;       // workspace: LF_DEV_* bits
+  uint32_t* queue;        // workspace: [2] single-split work-item counter, finished workgroups
   float* part_ml;         // workspace: [pairs][nsplit][GP][2]
   float* part_o;          // workspace: [pairs][nsplit][GP][d]
   float* ws_logit;        // workspace: [pairs][S][GP]
@@ -47,13 +48,15 @@ struct TopkParams {
 
 // team_grid > 0: after zeroing the team exchange words, one launch of the
 // team kernel with one workgroup per (pair, split), nblocks in all;
-// otherwise nblocks workgroups of the single-split kernel or of the split
-// kernel followed by the combine and finalize kernels.
+// otherwise, with one split, `grid` persistent workgroups of the
+// single-split kernel that take the nblocks pairs from the work-item counter,
+// or, with several, nblocks workgroups of the split kernel followed by the
+// combine and finalize kernels.
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
-                         int team_grid, hipStream_t stream);
-// Workgroups of the team kernel for (d, gp, nw, lds) that one compute unit
-// holds at once.
-hipError_t team_blocks_per_cu(int d, int gp, int nw, size_t lds, int* blocks);
+                         int team_grid, int grid, hipStream_t stream);
+// Workgroups of the team kernel (team = true) or of the single-split kernel
+// for (d, gp, nw, lds) that one compute unit holds at once.
+hipError_t decode_blocks_per_cu(bool team, int d, int gp, int nw, size_t lds, int* blocks);
 
 // One decode step after validation (the decode kernel and, for several
 // splits, the combine and finalize kernels).  mask_w non-null selects the

@@ -218,7 +218,7 @@ static bool device_holds_teams(int d, int gp, int nw, size_t lds, int nsplit_eff
   if (nsplit_eff < 2 || nsplit_eff > lf::kMaxTeamSplits) return false;
   int per_cu = 0, cus = 0;
   if (lf_device_num_cus(&cus) != LF_OK) return false;
-  if (lf::team_blocks_per_cu(d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return false;
+  if (lf::decode_blocks_per_cu(true, d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return false;
   return (int64_t)per_cu * cus > (int64_t)lf::kTicketRanges * (nsplit_eff - 1);
 }
 
@@ -249,6 +249,7 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
   prm.scores = scores;
   prm.evict = evict_slot;
   prm.status = reinterpret_cast<uint32_t*>(ws + wl.status);
+  prm.queue = reinterpret_cast<uint32_t*>(ws + wl.queue);
   prm.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
   prm.part_o = reinterpret_cast<float*>(ws + wl.part_o);
   prm.ws_logit = reinterpret_cast<float*>(ws + wl.logit);
@@ -280,7 +281,18 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
     prm.xticket = reinterpret_cast<uint32_t*>(ws + tl.xticket);
     prm.team_words = tl.zero_words;
   }
-  return lf::launch_decode(prm, d, gp, nw, nblocks, lds, team_grid, static_cast<hipStream_t>(stream)) ==
+  // One split: as many persistent workgroups as the device holds at once
+  // (fewer when there are fewer pairs); they take the pairs from the
+  // work-item counter.
+  int grid = 0;
+  if (eff == 1) {
+    int per_cu = 0, cus = 0;
+    if (lf_device_num_cus(&cus) != LF_OK) return LF_E_HIP;
+    if (lf::decode_blocks_per_cu(false, d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return LF_E_HIP;
+    const int64_t resident = (int64_t)per_cu * cus;
+    grid = (int)(resident < nblocks ? resident : nblocks);
+  }
+  return lf::launch_decode(prm, d, gp, nw, nblocks, lds, team_grid, grid, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? LF_OK
              : LF_E_HIP;

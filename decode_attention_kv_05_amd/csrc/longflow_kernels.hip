@@ -281,7 +281,10 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
 
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int tid = threadIdx.x;
+  // (opaque to the compiler, so that what derives from the thread index is
+  // computed for each pair and not kept live across the persistent loop)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int c = lane % LPR;   // 16-byte column chunk of the row
@@ -693,21 +696,59 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   }
 }
 
+// The kernel's parameter block read from the kernarg segment through a
+// pointer the compiler cannot follow (so the loads are not hoisted out of a
+// loop around the call).
+__device__ __forceinline__ DecodeParams reload_params() {
+  static_assert(sizeof(DecodeParams) % 4 == 0, "copied as 32-bit words");
+  auto pk = (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(pk));
+  DecodeParams q;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(&q);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(DecodeParams) / 4); ++i) dst[i] = pk[i];
+  return q;
+}
+
 template <int D, int GP, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_kernel(DecodeParams p) {
-  // Workgroups are dispatched round-robin over the 8 XCDs.  With one split
-  // per pair the pairs follow that order, so with 8 KV heads every XCD gets
-  // one head of every sequence and the same work whatever the sequences'
-  // lengths (ragged: 827.6 -> 815.7 us against contiguous runs per XCD).  The
-  // split mode gives each XCD a contiguous run of work items, so the splits
-  // of a pair share an L2; the team mode takes its items from a counter.
-  const int nblk = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int per = nblk >> 3, rem = nblk & 7;
-  const int item = MODE == kModeSingle ? (int)blockIdx.x
-                                       : xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
-  const int nsplit = MODE == kModeSingle ? 1 : p.nsplit;
-  if constexpr (MODE == kModeTeam) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* tk = reinterpret_cast<int*>(smem + lds_layout(D, GP, p.split_len, NW).scratch + kTicketSlot);
+  if constexpr (MODE == kModeSingle) {
+    // Persistent workgroups: workgroup w takes pair w first, then further
+    // pairs from the work-item counter (tickets gridDim.x, gridDim.x + 1, ...)
+    // until none is left, so a compute unit that streams faster takes more
+    // pairs.  (The dispatcher deals workgroups to the 8 XCDs in turn, and the
+    // XCDs stream at different rates: with one workgroup per pair, qwen3_8b's
+    // first pairs took 105 us on the fastest XCDs and 140 us on the slowest,
+    // and the ragged batch's long sequences ended the step on slow XCDs.  The
+    // first pair goes by block index because 512 workgroups starting on one
+    // counter at once spread their starts over 5 us.)
+    //
+    // The parameters are read again for every pair through a pointer the
+    // compiler cannot follow across iterations; otherwise it keeps every
+    // parameter and everything derived from it live across the loop, and
+    // the registers the pair needs spill.
+    // With at least as many workgroups as pairs the counter is not used.
+    const bool dynamic = gridDim.x < (unsigned)p.pairs;
+    unsigned t = blockIdx.x;
+    while (t < (unsigned)p.pairs) {
+      const DecodeParams pp = reload_params();
+      decode_pair<D, GP, NW, MODE>(pp, (int)t, (int)t, 0, 1);
+      if (!dynamic) break;
+      __syncthreads();  // the pair is done with the LDS
+      if (threadIdx.x == 0) *tk = (int)(gridDim.x + atomicAdd(p.queue, 1u));
+      __syncthreads();
+      t = (unsigned)*tk;
+    }
+    // Every workgroup has made its last claim once all have counted
+    // themselves out, so the last one can leave the counters at zero for the
+    // next launch.
+    if (dynamic && threadIdx.x == 0 && atomicAdd(p.queue + 1, 1u) == gridDim.x - 1) {
+      atomicExch(p.queue, 0u);
+      atomicExch(p.queue + 1, 0u);
+    }
+  } else if constexpr (MODE == kModeTeam) {
     // Work items go out by tickets in the order workgroups start, not by
     // block index.  The pairs form kTicketRanges ranges of whole teams, each
     // with its own counter (zeroed with the exchange words); a workgroup
@@ -721,8 +762,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     // whenever the device holds more than that at once, whatever the
     // dispatch order.  (One counter for all made 256 workgroups queue on one
     // atomic as a wave of them started: 3-4% slower.)
-    extern __shared__ __align__(16) unsigned char smem[];
-    int* tk = reinterpret_cast<int*>(smem + lds_layout(D, GP, p.split_len, NW).scratch + kTicketSlot);
+    const int nsplit = p.nsplit;
     if (threadIdx.x == 0) {
       int claimed = -1;
       for (int k = 0; k < kTicketRanges && claimed < 0; ++k) {
@@ -740,7 +780,14 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     if (t < 0) return;  // not reached: one workgroup per item
     decode_pair<D, GP, NW, MODE>(p, t, t / nsplit, t % nsplit, nsplit);
   } else {
-    decode_pair<D, GP, NW, MODE>(p, item, item / nsplit, item % nsplit, nsplit);
+    // The split mode gives each XCD (workgroups are dealt to the 8 XCDs in
+    // turn) a contiguous run of work items, so the splits of a pair share an
+    // L2.
+    const int nblk = gridDim.x;
+    const int xcd = blockIdx.x & 7;
+    const int per = nblk >> 3, rem = nblk & 7;
+    const int item = xcd * per + (xcd < rem ? xcd : rem) + (blockIdx.x >> 3);
+    decode_pair<D, GP, NW, MODE>(p, item, item / p.nsplit, item % p.nsplit, p.nsplit);
   }
 }
 
@@ -947,7 +994,7 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
 // ------------------------------------------------------------------ launch
 
 template <int D, int GP, int NW>
-hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, int team_grid, hipStream_t stream) {
+hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, int team_grid, int grid, hipStream_t stream) {
   if (team_grid > 0) {
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(prm.xstat), prm.team_words, 0u, stream);
     if (e != hipSuccess) return e;
@@ -972,68 +1019,70 @@ hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, int team
     hipLaunchKernelGGL(longflow_finalize_kernel, dim3((pairs + 255) / 256), dim3(256), 0, stream,
                        prm, pairs, nchunk);
   } else {
-    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeSingle>), dim3(nblocks), dim3(NW * 64), lds,
+    hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeSingle>), dim3(grid), dim3(NW * 64), lds,
                        stream, prm);
   }
   return hipGetLastError();
 }
 
 template <int D, int GP>
-hipError_t launch_dg(const DecodeParams& prm, int nw, int nblocks, size_t lds, int team_grid, hipStream_t stream) {
-  if (nw == kWavesLargeLds) return launch_dgw<D, GP, kWavesLargeLds>(prm, nblocks, lds, team_grid, stream);
-  if (nw == kWavesSmallLds) return launch_dgw<D, GP, kWavesSmallLds>(prm, nblocks, lds, team_grid, stream);
+hipError_t launch_dg(const DecodeParams& prm, int nw, int nblocks, size_t lds, int team_grid, int grid,
+                     hipStream_t stream) {
+  if (nw == kWavesLargeLds) return launch_dgw<D, GP, kWavesLargeLds>(prm, nblocks, lds, team_grid, grid, stream);
+  if (nw == kWavesSmallLds) return launch_dgw<D, GP, kWavesSmallLds>(prm, nblocks, lds, team_grid, grid, stream);
   return hipErrorInvalidValue;
+}
+
+template <int D, int GP, int NW>
+hipError_t occupancy_dgw(bool team, size_t lds, int* blocks) {
+  const void* f = team ? reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, NW, kModeTeam>)
+                       : reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, NW, kModeSingle>);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, NW * 64, lds);
 }
 
 template <int D, int GP>
-hipError_t team_occupancy_dg(int nw, size_t lds, int* blocks) {
-  if (nw == kWavesLargeLds)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, kWavesLargeLds, kModeTeam>),
-        kWavesLargeLds * 64, lds);
-  if (nw == kWavesSmallLds)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, reinterpret_cast<const void*>(&longflow_decode_kernel<D, GP, kWavesSmallLds, kModeTeam>),
-        kWavesSmallLds * 64, lds);
+hipError_t occupancy_dg(bool team, int nw, size_t lds, int* blocks) {
+  if (nw == kWavesLargeLds) return occupancy_dgw<D, GP, kWavesLargeLds>(team, lds, blocks);
+  if (nw == kWavesSmallLds) return occupancy_dgw<D, GP, kWavesSmallLds>(team, lds, blocks);
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t team_occupancy_d(int gp, int nw, size_t lds, int* blocks) {
+hipError_t occupancy_d(bool team, int gp, int nw, size_t lds, int* blocks) {
   switch (gp) {
-    case 1: return team_occupancy_dg<D, 1>(nw, lds, blocks);
-    case 2: return team_occupancy_dg<D, 2>(nw, lds, blocks);
-    case 4: return team_occupancy_dg<D, 4>(nw, lds, blocks);
-    case 8: return team_occupancy_dg<D, 8>(nw, lds, blocks);
+    case 1: return occupancy_dg<D, 1>(team, nw, lds, blocks);
+    case 2: return occupancy_dg<D, 2>(team, nw, lds, blocks);
+    case 4: return occupancy_dg<D, 4>(team, nw, lds, blocks);
+    case 8: return occupancy_dg<D, 8>(team, nw, lds, blocks);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t team_blocks_per_cu(int d, int gp, int nw, size_t lds, int* blocks) {
+hipError_t decode_blocks_per_cu(bool team, int d, int gp, int nw, size_t lds, int* blocks) {
   switch (d) {
-    case 64: return team_occupancy_d<64>(gp, nw, lds, blocks);
-    case 128: return team_occupancy_d<128>(gp, nw, lds, blocks);
+    case 64: return occupancy_d<64>(team, gp, nw, lds, blocks);
+    case 128: return occupancy_d<128>(team, gp, nw, lds, blocks);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams& prm, int gp, int nw, int nblocks, size_t lds, int team_grid,
+hipError_t launch_d(const DecodeParams& prm, int gp, int nw, int nblocks, size_t lds, int team_grid, int grid,
                     hipStream_t stream) {
   switch (gp) {
-    case 1: return launch_dg<D, 1>(prm, nw, nblocks, lds, team_grid, stream);
-    case 2: return launch_dg<D, 2>(prm, nw, nblocks, lds, team_grid, stream);
-    case 4: return launch_dg<D, 4>(prm, nw, nblocks, lds, team_grid, stream);
-    case 8: return launch_dg<D, 8>(prm, nw, nblocks, lds, team_grid, stream);
+    case 1: return launch_dg<D, 1>(prm, nw, nblocks, lds, team_grid, grid, stream);
+    case 2: return launch_dg<D, 2>(prm, nw, nblocks, lds, team_grid, grid, stream);
+    case 4: return launch_dg<D, 4>(prm, nw, nblocks, lds, team_grid, grid, stream);
+    case 8: return launch_dg<D, 8>(prm, nw, nblocks, lds, team_grid, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode(const DecodeParams& prm, int d, int gp, int nw, int nblocks, size_t lds,
-                         int team_grid, hipStream_t stream) {
+                         int team_grid, int grid, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_d<64>(prm, gp, nw, nblocks, lds, team_grid, stream);
-    case 128: return launch_d<128>(prm, gp, nw, nblocks, lds, team_grid, stream);
+    case 64: return launch_d<64>(prm, gp, nw, nblocks, lds, team_grid, grid, stream);
+    case 128: return launch_d<128>(prm, gp, nw, nblocks, lds, team_grid, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

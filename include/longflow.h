@@ -55,6 +55,11 @@
  * lf_read_device_status.  Two calls that share a workspace must be ordered on
  * one stream.
  *
+ * Workspace: zero-filled before its first use (lf_workspace_init, or any
+ * zeroing of the memory).  It holds the device status word and the work-item
+ * counters of the one-split step, which every call leaves at zero for the
+ * next; everything else in it is scratch for the duration of a call.
+ *
  * Errors: every entry point returns LF_OK (0) or a negative lf_status code
  * from host-side checks made before anything is enqueued; nothing is enqueued
  * on error.  Conditions that depend on device-resident values (prev_slot)
@@ -146,8 +151,8 @@ int lf_workspace_size(int B, int Hq, int Hkv, int d, int S, int nsplit, size_t* 
 int lf_device_num_cus(int* num_cus);
 
 /* Zero the workspace (its status word included) with a fill kernel enqueued
- * on `stream`.  Needed only to clear recorded LF_DEV_* bits: no other
- * workspace content carries over from one call to the next. */
+ * on `stream`: before the first use of a workspace that was not allocated
+ * zeroed, and to clear recorded LF_DEV_* bits. */
 int lf_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only argument validation, exactly the checks longflow_decode_nsplit
