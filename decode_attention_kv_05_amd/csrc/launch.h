@@ -63,11 +63,13 @@ hipError_t decode_blocks_per_cu(bool team, int d, int gp, int nw, size_t lds, in
 // fill step.  evict_slot may equal prev_slot outside the fill step: every
 // split reads its pair's prev_slot before the pair's evicted slot is
 // written (by the same workgroup at its end, or by the finalize kernel).
+// team_only: the workspace holds only what a team-path step touches (a
+// split step then takes the team path or fails with LF_E_NSPLIT).
 int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
                         void* k_cache, void* v_cache, const uint8_t* mask, uint8_t* mask_w,
                         const void* new_k, const void* new_v, const int32_t* prev_slot, void* out,
                         float* scores, int32_t* evict_slot, void* workspace, int nsplit,
-                        int split_path, void* stream);
+                        int split_path, void* stream, bool team_only = false);
 hipError_t launch_topk(const TopkParams& prm, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 

@@ -80,6 +80,9 @@ LF_HD inline size_t team_region_bytes(size_t pairs, int nsplit_eff, int gp, int 
 constexpr int kCombineSlots = 2048;
 LF_HD inline int combine_chunks(int S) { return (S + kCombineSlots - 1) / kCombineSlots; }
 
+// The status word and the work-item counters first, then (several splits)
+// the team exchange region, then the combine path's arrays: a team-path step
+// touches only the first team_workspace_bytes of the workspace.
 LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int gp, int nsplit_eff) {
   WorkspaceLayout w{};
   const size_t pairs = (size_t)B * (size_t)Hkv;
@@ -87,6 +90,8 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
   w.status = 0;
   w.queue = 16;
   if (nsplit_eff > 1) {
+    w.team = off;
+    off = align_up(off + team_region_bytes(pairs, nsplit_eff, gp, d), 256);
     w.part_ml = off;
     off = align_up(off + pairs * nsplit_eff * gp * 2 * 4, 256);
     w.part_o = off;
@@ -99,13 +104,18 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
     off = align_up(off + pairs * (size_t)combine_chunks(S) * 8, 256);
     w.ffree = off;
     off = align_up(off + pairs * (size_t)combine_chunks(S) * 4, 256);
-    w.team = off;
-    off = align_up(off + team_region_bytes(pairs, nsplit_eff, gp, d), 256);
   } else {
     w.part_ml = w.part_o = w.logit = w.vnorm = w.cand = w.ffree = w.team = off;
   }
   w.total = off;
   return w;
+}
+
+// Bytes of the workspace a step touches on the team path (header and team
+// region), or with one split (header only).
+LF_HD inline size_t team_workspace_bytes(int B, int Hkv, int d, int gp, int nsplit_eff) {
+  if (nsplit_eff < 2) return 256;
+  return align_up(256 + team_region_bytes((size_t)B * (size_t)Hkv, nsplit_eff, gp, d), 256);
 }
 
 // Words of the team region, in this order: published split (max, sum) per

@@ -8,6 +8,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "launch.h"
 #include "layout.h"
@@ -56,6 +57,7 @@ const char* lf_strerror(int code) {
     case LF_E_HIP: return "HIP runtime call or kernel launch failed";
     case LF_E_NSPLIT: return "slot split count not usable for this shape";
     case LF_E_VALUE: return "non-finite scale";
+    case LF_E_SCRATCH: return "the step needs more scratch memory than the library's static buffer holds";
     default: return "unknown longflow status code";
   }
 }
@@ -152,11 +154,12 @@ namespace {
 
 // The checks of lf_validate; `mask_written` marks the fill step, which
 // updates the mask in place (so it must not overlap any other buffer).
+// `team_only`: the workspace need only hold what a team-path step touches.
 int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
                   const void* k_cache, const void* v_cache, const uint8_t* mask, const void* new_k,
                   const void* new_v, const int32_t* prev_slot, const void* out, const float* scores,
                   const int32_t* evict_slot, const void* workspace, size_t workspace_bytes,
-                  int nsplit, bool mask_written) {
+                  int nsplit, bool mask_written, bool team_only = false) {
   int rc = lf_check_shape(B, Hq, Hkv, d, S);
   if (rc != LF_OK) return rc;
   if (!std::isfinite(scale)) return LF_E_VALUE;
@@ -183,7 +186,8 @@ int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void*
   const size_t row_bytes = pairs * d * 2;
   const size_t idx_bytes = pairs * 4;
   const size_t score_bytes = pairs * S * 4;
-  const size_t ws_need = lf::workspace_layout(B, Hkv, d, S, gp, eff).total;
+  const size_t ws_need = team_only ? lf::team_workspace_bytes(B, Hkv, d, gp, eff)
+                                   : lf::workspace_layout(B, Hkv, d, S, gp, eff).total;
 
   struct Buf {
     const void* p;
@@ -227,7 +231,8 @@ static bool device_holds_teams(int d, int gp, int nw, size_t lds, int nsplit_eff
 int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q, void* k_cache,
                  void* v_cache, const uint8_t* mask, uint8_t* mask_w, const void* new_k,
                  const void* new_v, const int32_t* prev_slot, void* out, float* scores,
-                 int32_t* evict_slot, void* workspace, int nsplit, int split_path, void* stream) {
+                 int32_t* evict_slot, void* workspace, int nsplit, int split_path, void* stream,
+                 bool team_only) {
   const int G = Hq / Hkv;
   const int gp = lf::padded_group(G);
   int len, eff;
@@ -256,6 +261,14 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
   prm.ws_vnorm = reinterpret_cast<float*>(ws + wl.vnorm);
   prm.cand = reinterpret_cast<uint64_t*>(ws + wl.cand);
   prm.ffree = reinterpret_cast<uint32_t*>(ws + wl.ffree);
+  if (team_only) {
+    // The workspace ends after the team region: the combine path's arrays
+    // are not there (the team path and the one-split step never use them).
+    prm.part_ml = prm.part_o = prm.ws_logit = prm.ws_vnorm = nullptr;
+    prm.cand = nullptr;
+    prm.ffree = nullptr;
+    if (eff > 1) split_path = LF_SPLIT_TEAM;
+  }
   prm.Hq = Hq;
   prm.Hkv = Hkv;
   prm.G = G;
@@ -425,3 +438,70 @@ int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags) 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation entry point
+//
+// longflow_decode_noalloc keeps its workspace in `scratch`, a device array of
+// the library: one per GPU the library runs on, alive until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory, so its device address is looked up once per device (with that
+// device current) and only that address is used.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[LF_STATIC_SCRATCH_BYTES];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, or null.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int longflow_decode_noalloc(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
+                                       void* k_cache, void* v_cache, const uint8_t* mask, const void* new_k,
+                                       const void* new_v, const int32_t* prev_slot, void* out, float* scores,
+                                       int32_t* evict_slot, void* stream) {
+  int rc = lf_check_shape(B, Hq, Hkv, d, S);
+  if (rc != LF_OK) return rc;
+  if (B == 0) return std::isfinite(scale) ? LF_OK : LF_E_VALUE;
+  int cus = 0, nsplit = 1;
+  if ((rc = lf_device_num_cus(&cus)) != LF_OK) return rc;
+  if ((rc = lf_plan_nsplit(B, Hq, Hkv, d, S, cus, &nsplit)) != LF_OK) return rc;
+  // What the step touches: the header with one split; the header and the
+  // team region on the team path; else the whole combine layout.
+  const int gp = lf::padded_group(Hq / Hkv);
+  int len, eff;
+  lf::split_geometry(S, nsplit, &len, &eff);
+  bool team_only = false;
+  size_t need = 256;
+  if (eff > 1) {
+    const int nw = lf::decode_waves(gp, len);
+    const size_t lds = lf::lds_layout(d, gp, len, nw).total;
+    team_only = lf::device_holds_teams(d, gp, nw, lds, eff);
+    need = team_only ? lf::team_workspace_bytes(B, Hkv, d, gp, eff)
+                     : lf::workspace_layout(B, Hkv, d, S, gp, eff).total;
+  }
+  if (need > (size_t)LF_STATIC_SCRATCH_BYTES) return LF_E_SCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return LF_E_HIP;
+  rc = validate_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v, prev_slot, out, scores,
+                     evict_slot, ws, (size_t)LF_STATIC_SCRATCH_BYTES, nsplit, false, team_only);
+  if (rc != LF_OK) return rc;
+  // The previous call on this device left its status bits and counters
+  // here; this call starts from zero (a fill kernel, so the call can be
+  // recorded into a graph).
+  if (lf::launch_fill_u32(static_cast<uint32_t*>(ws), 64, 0u, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LF_E_HIP;
+  return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, nullptr, new_k, new_v,
+                                 prev_slot, out, scores, evict_slot, ws, nsplit, LF_SPLIT_AUTO, stream, team_only);
+}

@@ -22,6 +22,7 @@ LF_E_WORKSPACE = -5
 LF_E_HIP = -6
 LF_E_NSPLIT = -7
 LF_E_VALUE = -8
+LF_E_SCRATCH = -9
 
 LF_DEV_BAD_PREV = 0x1
 LF_DEV_WRITE_MASKED = 0x2
@@ -35,7 +36,7 @@ EXPORTED = (
     "lf_version", "lf_source_hash", "lf_strerror", "lf_check_shape", "lf_plan_nsplit", "lf_workspace_size",
     "lf_device_num_cus", "lf_workspace_init", "lf_validate", "longflow_decode",
     "longflow_decode_nsplit", "longflow_decode_fill", "longflow_decode_ex", "longflow_evict_topk",
-    "lf_read_device_status",
+    "lf_read_device_status", "longflow_decode_noalloc",
     "lf_stack_workspace_size", "lf_stack_workspace_offsets", "longflow_stack_step", "lf_stack_graph_create", "lf_graph_launch",
     "lf_graph_destroy",
 )
@@ -63,6 +64,7 @@ def _load():
         "longflow_decode_ex": ([_i] * 5 + [_f] + [_p] * 4 + [_i] + [_p] * 7 + [_sz, _i, _i, _p], _i),
         "longflow_evict_topk": ([_i] * 4 + [_p] * 3 + [_p], _i),
         "lf_read_device_status": ([_p, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
+        "longflow_decode_noalloc": ([_i] * 5 + [_f] + [_p] * 10 + [_p], _i),
         "lf_stack_workspace_size": ([_i] * 8 + [ctypes.POINTER(_sz)], _i),
         "lf_stack_workspace_offsets": ([_i] * 7 + [ctypes.POINTER(_sz)], _i),
         "longflow_stack_step": ([_i] * 7 + [_f, _f] + [_p] * 3 + [_i] + [_p] * 8 + [_sz, _i, _p], _i),
@@ -93,7 +95,8 @@ class LongflowError(RuntimeError):
 
 def _check(rc, where):
     if rc != LF_OK:
-        if rc in (LF_E_SHAPE, LF_E_ALIGN, LF_E_ALIAS, LF_E_NULL, LF_E_NSPLIT, LF_E_VALUE, LF_E_WORKSPACE):
+        if rc in (LF_E_SHAPE, LF_E_ALIGN, LF_E_ALIAS, LF_E_NULL, LF_E_NSPLIT, LF_E_VALUE, LF_E_WORKSPACE,
+                  LF_E_SCRATCH):
             raise ValueError(f"{where}: {lf_strerror(rc)} (code {rc})")
         raise LongflowError(rc, where)
 
@@ -273,6 +276,32 @@ def longflow_decode_fill(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, *, 
     """
     return _step("longflow_decode_fill", q, k_cache, v_cache, mask, new_k, new_v, prev_slot, scale, out,
                  scores, next_slot, workspace, nsplit, stream, split_path, check)
+
+
+def longflow_decode_noalloc(q, k_cache, v_cache, mask, new_k, new_v, prev_slot, out, scores, evict_slot, *,
+                            scale=None, stream=None):
+    """longflow_decode with the library's static scratch array as its
+    workspace (include/longflow.h): the caller passes every output, nothing
+    is allocated.  Calls on one GPU must not overlap in time."""
+    B, Hq, d = q.shape
+    Hkv, S = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    for t, name, dt, shape in ((q, "q", torch.bfloat16, (B, Hq, d)), (k_cache, "k_cache", torch.bfloat16, (B, Hkv, S, d)),
+                               (v_cache, "v_cache", torch.bfloat16, (B, Hkv, S, d)),
+                               (mask, "mask", (torch.uint8, torch.bool), (B, S)),
+                               (new_k, "new_k", torch.bfloat16, (B, Hkv, d)), (new_v, "new_v", torch.bfloat16, (B, Hkv, d)),
+                               (prev_slot, "prev_slot", torch.int32, (B, Hkv)), (out, "out", torch.bfloat16, (B, Hq, d)),
+                               (scores, "scores", torch.float32, (B, Hkv, S)),
+                               (evict_slot, "evict_slot", torch.int32, (B, Hkv))):
+        _need(t, name, dt, shape, dev)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = _lib.longflow_decode_noalloc(B, Hq, Hkv, d, S, float(scale), ptr(q), ptr(k_cache), ptr(v_cache), ptr(mask),
+                                      ptr(new_k), ptr(new_v), ptr(prev_slot), ptr(out), ptr(scores), ptr(evict_slot),
+                                      _stream_ptr(stream, dev))
+    _check(rc, "longflow_decode_noalloc")
+    return out, scores, evict_slot
 
 
 def longflow_evict_topk(scores, mask, k, *, out=None, stream=None):

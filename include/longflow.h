@@ -89,7 +89,9 @@ typedef enum lf_status {
   LF_E_WORKSPACE = -5,  /* workspace too small                                 */
   LF_E_HIP = -6,        /* a HIP runtime call or kernel launch failed          */
   LF_E_NSPLIT = -7,     /* requested slot split count not usable for the shape */
-  LF_E_VALUE = -8       /* non-finite scale                                    */
+  LF_E_VALUE = -8,      /* non-finite scale                                    */
+  LF_E_SCRATCH = -9     /* longflow_decode_noalloc: the step needs more than
+                           LF_STATIC_SCRATCH_BYTES of scratch                  */
 } lf_status;
 
 /* Device status bits, accumulated in the workspace across calls until cleared. */
@@ -256,6 +258,35 @@ int longflow_evict_topk(int B, int Hkv, int S, int k, const float* scores,
 
 /* Copy the workspace's LF_DEV_* bits to *flags.  Synchronises `stream`. */
 int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags);
+
+/* Size of the device array that longflow_decode_noalloc uses as its
+ * workspace: 16 MiB, one array per GPU the library runs on, held until the
+ * process ends. */
+#define LF_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* longflow_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * may not call hipMalloc, harnesses that forbid allocation.  Same operator,
+ * arguments, shapes, plan and results as longflow_decode (the same kernels);
+ * the workspace is the library's own LF_STATIC_SCRATCH_BYTES device array,
+ * cleared (by a fill kernel on `stream`) at the start of every call.  The
+ * call allocates nothing and makes no allocating library call; the array's
+ * device address is looked up on the first call on each device.
+ * A step that needs more scratch than the array holds returns LF_E_SCRATCH
+ * before anything is enqueued: a one-split step needs 256 bytes; a split step
+ * on the team path 256 bytes plus its exchange region (about 8.3 KB per
+ * (sequence, KV head) and split at 8 query heads per KV head and d = 128:
+ * 4.3 MB for 16 x 8 pairs in 4 splits); a split step that cannot take the
+ * team path, its whole combine workspace (lf_workspace_size).
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (other streams, other threads of the process) race and give
+ * unspecified results; order them on one stream.  The device status bits
+ * are not reported (use longflow_decode with a workspace to read them). */
+int longflow_decode_noalloc(int B, int Hq, int Hkv, int d, int S, float scale,
+                            const void* q, void* k_cache, void* v_cache,
+                            const uint8_t* mask, const void* new_k, const void* new_v,
+                            const int32_t* prev_slot, void* out, float* scores,
+                            int32_t* evict_slot, void* stream);
 
 #ifdef __cplusplus
 }
