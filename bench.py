@@ -288,12 +288,25 @@ def timed(step, K, Wm, stream, dev, reset=None):
     return np.array(reps), per_launch, wall, warm
 
 
-def hbm_probes(dev, nbytes=1 << 30, reps=5):
-    """The GPU's practical HBM rates on this machine, from plain torch kernels
-    (not the library): a device-to-device copy of nbytes (read + write
-    bytes per second) and a read-only reduction over nbytes (read bytes per
-    second); median of `reps` event-timed runs each."""
+def hbm_probes(dev, k_cache=None, v_cache=None, reps=5):
+    """The GPU's practical HBM read rates on this machine, measured in the same
+    run by plain read kernels (libhbm_probe.so, not the library): the whole
+    grid reading in address order, and the decode's own pattern without its
+    arithmetic (K then V of each (sequence, KV head) pair, one workgroup per
+    pair) over the run's caches; plus a torch device-to-device copy (read +
+    write bytes).  Median of `reps` event-timed runs each, GB/s."""
+    import ctypes
+
     import torch
+
+    from decode_attention_kv_05_amd.build import PROBE_PATH
+    lib = ctypes.CDLL(PROBE_PATH)
+    lib.lf_probe_read_interleaved.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lf_probe_read_pairs.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    nbytes = 1 << 30
     src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
 
@@ -310,9 +323,22 @@ def hbm_probes(dev, nbytes=1 << 30, reps=5):
             ts.append(a.elapsed_time(b) / 1e3)
         return round(moved / float(np.median(ts)) / 1e9, 1)
 
-    out = {"copy_GBps": rate(lambda: dst.copy_(src), 2 * nbytes),
-           "read_GBps": rate(lambda: src.sum(dtype=torch.float32), nbytes),
-           "bytes": nbytes, "how": "torch copy_ and sum over 1 GiB of bf16, median of 5"}
+    def call(rc):
+        if rc != 0:
+            raise RuntimeError("probe launch failed")
+
+    out = {"read_interleaved_GBps": rate(lambda: call(lib.lf_probe_read_interleaved(src.data_ptr(), nbytes,
+                                                                                     sink.data_ptr(), stream)), nbytes),
+           "copy_GBps": rate(lambda: dst.copy_(src), 2 * nbytes)}
+    if k_cache is not None:
+        B, Hkv, S, d = k_cache.shape
+        pb = S * d * 2
+        out["read_pairs_GBps"] = rate(lambda: call(lib.lf_probe_read_pairs(k_cache.data_ptr(), v_cache.data_ptr(),
+                                                                           B * Hkv, pb, sink.data_ptr(), stream)),
+                                      2 * B * Hkv * pb)
+    out["how"] = ("read_interleaved: 1 GiB read by the whole grid in address order; read_pairs: the run's K then V "
+                  "caches, one 8-wave workgroup per pair, the decode's loads without its arithmetic; copy: torch "
+                  "copy_ of 1 GiB (read + write); median of 5")
     del src, dst
     return out
 
@@ -517,7 +543,7 @@ def main():
                    "warmup_steps_run": warm, "warmup_min_s": WARMUP_MIN_S},
         "wall_s_timed": round(wall, 3),
     }
-    result["hbm_probe"] = hbm_probes(dev)
+    result["hbm_probe"] = hbm_probes(dev, dk, dv)
     if args.mode == "fill":
         result["config"].update({"mode": "fill", "start_valid_slots": fill_from})
     if args.mode == "cadence":

@@ -16,6 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblongflow.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# Read-bandwidth probes used by the benchmark only (not part of the library).
+PROBE_PATH = os.path.join(HERE, "libhbm_probe.so")
+PROBE_SOURCE = os.path.join(CSRC, "hbm_probe.hip")
 SOURCES = [os.path.join(CSRC, n) for n in ("longflow_api.cpp", "longflow_kernels.hip", "evict_topk.hip",
                                             "stack_api.cpp", "stack_kernels.hip")]
 ARCH = "gfx950"
@@ -87,6 +90,18 @@ def compile_command(out_path):
     ]
 
 
+def build_probe():
+    """Compile the benchmark's read probes (libhbm_probe.so)."""
+    tmp = PROBE_PATH + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *CODEGEN_FLAGS, "-Wall", PROBE_SOURCE, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
+
+
 def build(verbose=False):
     """Compile the library (always) and return its path."""
     tmp = LIB_PATH + f".tmp{os.getpid()}"
@@ -106,11 +121,15 @@ def build(verbose=False):
 
 def ensure_built():
     """Path of the built library, building it when it is absent or was built
-    from other sources than the current ones."""
+    from other sources than the current ones (and the probe library when it
+    is absent or older than its source)."""
     if built_hash() != source_hash():
         build()
+    if not os.path.exists(PROBE_PATH) or os.path.getmtime(PROBE_PATH) < os.path.getmtime(PROBE_SOURCE):
+        build_probe()
     return LIB_PATH
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe())

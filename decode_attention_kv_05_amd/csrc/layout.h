@@ -148,14 +148,17 @@ LF_HD inline TeamLayout team_layout(const WorkspaceLayout& w, int B, int Hkv, in
 struct LdsLayout {
   size_t logits;  // float [split_len + kRowPad][GP]; reused for the cross-wave O reduction
   size_t mask;    // uint8 [split_len + kRowPad], zero past the split
+  size_t vnorm;   // team: float [split_len + kRowPad], |v|_1 per row (empty otherwise)
   size_t scratch; // reductions and broadcast values
   size_t total;
 };
 
 constexpr size_t kScratchBytes = 1024;
-// Offset in the scratch area of the team kernel's work-item ticket; the
-// decode body's reductions use the bytes below it.
+// Offsets in the scratch area of the work-item ticket and of the counter
+// that hands phase-K batches to the waves; the decode body's reductions use
+// the bytes below them.
 constexpr size_t kTicketSlot = kScratchBytes - 16;
+constexpr size_t kBatchSlot = kScratchBytes - 12;
 // Rows past the end of a split that a wave batch may touch; the mask and
 // logit arrays are padded by this much so those reads need no bounds check.
 constexpr int kRowPad = 128;
@@ -163,16 +166,7 @@ constexpr int kRowPad = 128;
 // LDS a workgroup may use so that two of them share a compute unit.
 constexpr size_t kHalfLdsBytes = 80 * 1024;
 
-// Wavefronts per decode workgroup for a split: a workgroup whose logits
-// leave room for a second one on the CU gets fewer waves, so that two of
-// them (which reach their barriers independently) share the CU.
-LF_HD inline int decode_waves(int gp, int split_len) {
-  return (size_t)(split_len + kRowPad) * gp * 4 + split_len + kRowPad + kScratchBytes > kHalfLdsBytes
-             ? kWavesLargeLds
-             : kWavesSmallLds;
-}
-
-LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len, int nw) {
+LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len, int nw, bool team = false) {
   LdsLayout l{};
   size_t logits = align_up((size_t)(split_len + kRowPad) * gp * 4, 16);
   size_t ored = (size_t)nw * gp * d * 4;
@@ -180,19 +174,30 @@ LF_HD inline LdsLayout lds_layout(int d, int gp, int split_len, int nw) {
   size_t off = logits > ored ? logits : ored;
   l.mask = off;
   off = align_up(off + split_len + kRowPad, 16);
+  l.vnorm = off;
+  if (team) off = align_up(off + (size_t)(split_len + kRowPad) * 4, 16);
   l.scratch = off;
   l.total = off + kScratchBytes;
   return l;
+}
+
+// Wavefronts per decode workgroup for a split: a workgroup whose logits
+// leave room for a second one on the CU gets fewer waves, so that two of
+// them (which reach their barriers independently) share the CU.
+LF_HD inline int decode_waves(int gp, int split_len, bool team = false) {
+  const size_t rows = (size_t)(split_len + kRowPad);
+  return rows * gp * 4 + rows + kScratchBytes + (team ? rows * 4 : 0) > kHalfLdsBytes ? kWavesLargeLds
+                                                                                      : kWavesSmallLds;
 }
 
 // LDS of one compute unit on gfx950; a workgroup may use all of it.
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 // Longest split whose logits fit the budget and whose whole LDS layout fits
-// the compute unit.
-LF_HD inline int max_split_len(int d, int gp) {
+// the compute unit (on the team path, with its |v|_1 row as well).
+LF_HD inline int max_split_len(int d, int gp, bool team = false) {
   int len = (int)(kLogitLdsBudget / ((size_t)gp * 4));
-  while (len > 0 && lds_layout(d, gp, len, kMaxWaves).total > kMaxLdsBytes) len -= 64;
+  while (len > 0 && lds_layout(d, gp, len, kMaxWaves, team).total > kMaxLdsBytes) len -= 64;
   return len;
 }
 

@@ -93,6 +93,10 @@ int lf_plan_nsplit(int B, int Hq, int Hkv, int d, int S, int num_cus, int* nspli
     const int64_t cap = ((int64_t)S + 255) / 256;
     if (target > n) n = target < cap ? target : cap;
     if (n < need) n = need;
+    // Splits short enough for the team path, which also keeps |v|_1 per row.
+    const int team_len = lf::max_split_len(d, gp, true);
+    const int64_t team_need = ((int64_t)S + team_len - 1) / team_len;
+    if (n > 1 && n < team_need) n = team_need;
   }
   if (n < 1) n = 1;
   if (n > lf::kMaxSplits) return LF_E_SHAPE;
@@ -279,14 +283,20 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
   prm.qscale = scale * 1.4426950408889634f;
 
   const int nblocks = B * Hkv * eff;
-  const int nw = lf::decode_waves(gp, len);
-  const size_t lds = lf::lds_layout(d, gp, len, nw).total;
+  int nw = lf::decode_waves(gp, len);
+  size_t lds = lf::lds_layout(d, gp, len, nw).total;
   prm.pairs = B * Hkv;
   int team_grid = 0;
   if (eff > 1 && split_path != LF_SPLIT_COMBINE) {
     const lf::TeamLayout tl = lf::team_layout(wl, B, Hkv, d, gp, eff);
-    team_grid = device_holds_teams(d, gp, nw, lds, eff) ? nblocks : 0;
+    const int nw_team = lf::decode_waves(gp, len, true);
+    const size_t lds_team = lf::lds_layout(d, gp, len, nw_team, true).total;
+    team_grid = lds_team <= lf::kMaxLdsBytes && device_holds_teams(d, gp, nw_team, lds_team, eff) ? nblocks : 0;
     if (team_grid == 0 && split_path == LF_SPLIT_TEAM) return LF_E_NSPLIT;
+    if (team_grid > 0) {
+      nw = nw_team;
+      lds = lds_team;
+    }
     prm.xstat = reinterpret_cast<uint64_t*>(ws + tl.xstat);
     prm.xfin = reinterpret_cast<uint64_t*>(ws + tl.xfin);
     prm.xo = reinterpret_cast<uint64_t*>(ws + tl.xo);
@@ -485,9 +495,9 @@ extern "C" int longflow_decode_noalloc(int B, int Hq, int Hkv, int d, int S, flo
   bool team_only = false;
   size_t need = 256;
   if (eff > 1) {
-    const int nw = lf::decode_waves(gp, len);
-    const size_t lds = lf::lds_layout(d, gp, len, nw).total;
-    team_only = lf::device_holds_teams(d, gp, nw, lds, eff);
+    const int nw = lf::decode_waves(gp, len, true);
+    const size_t lds = lf::lds_layout(d, gp, len, nw, true).total;
+    team_only = lds <= lf::kMaxLdsBytes && lf::device_holds_teams(d, gp, nw, lds, eff);
     need = team_only ? lf::team_workspace_bytes(B, Hkv, d, gp, eff)
                      : lf::workspace_layout(B, Hkv, d, S, gp, eff).total;
   }

@@ -156,6 +156,51 @@ __device__ __forceinline__ float allreduce_sum(float x) {
   }
 }
 
+// Sum of each of N = GP * 8 accumulators over the row groups of a wave
+// (the lanes that share a column chunk: lane bits 5, 4 and, for 8-lane rows,
+// 3), left scattered: afterwards the first N / RG entries of a (RG = 64 /
+// LPR row groups) hold the sums of entries fold_base(lane) .. + N / RG - 1.
+// Bits 5 and 4 go through gfx950's lane swaps in the VALU: after
+// permlane32_swap(x, y), lanes 0-31 hold (x_l, x_{l+32}) and lanes 32-63
+// (y_{l-32}, y_l), so adding the pair leaves x's sum in the lower half and
+// y's in the upper half; permlane16_swap does the same within each half.
+template <int LPR, int GP>
+__device__ __forceinline__ void fold_row_groups(float (&a)[GP][8], int lane) {
+  constexpr int N = GP * 8;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const int j = N / 2 + i;
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i / 8][i % 8]), __float_as_uint(a[j / 8][j % 8]),
+                                                    false, false);
+    a[i / 8][i % 8] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const int j = N / 4 + i;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i / 8][i % 8]), __float_as_uint(a[j / 8][j % 8]),
+                                                    false, false);
+    a[i / 8][i % 8] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (LPR == 8) {
+    const bool upper = (lane & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const int j = N / 8 + i;
+      const float send = upper ? a[i / 8][i % 8] : a[j / 8][j % 8];
+      const float keep = upper ? a[j / 8][j % 8] : a[i / 8][i % 8];
+      a[i / 8][i % 8] = keep + partner<8>(send);
+    }
+  }
+}
+
+template <int LPR, int GP>
+__device__ __forceinline__ int fold_base(int lane) {
+  constexpr int N = GP * 8;
+  int base = (lane >> 5) * (N / 2) + ((lane >> 4) & 1) * (N / 4);
+  if constexpr (LPR == 8) base += ((lane >> 3) & 1) * (N / 8);
+  return base;
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)x, m);
   const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), m);
@@ -295,17 +340,19 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   const int s0 = sp * p.split_len;
   const int n = min(p.S, s0 + p.split_len) - s0;
 
-  const LdsLayout L = lds_layout(D, GP, p.split_len, NW);
+  const LdsLayout L = lds_layout(D, GP, p.split_len, NW, TEAM);
   float* lg = reinterpret_cast<float*>(smem + L.logits);
   uint8_t* mk = smem + L.mask;
+  float* vnl = reinterpret_cast<float*>(smem + L.vnorm);         // team: |v|_1 per row
   float* red = reinterpret_cast<float*>(smem + L.scratch);     // [NW][GP]
-  float* stat_m = red + NW * GP;                                 // [GP]
-  float* stat_il = stat_m + GP;                                  // [GP] 1 / L
-  uint64_t* best_w = reinterpret_cast<uint64_t*>(stat_il + GP);  // [NW]
+  float* stat_m = red + NW * GP;                                 // [GP] split max (team: then the pair's)
+  float* stat_il = stat_m + GP;                                  // [GP] 1 / L (team: the pair's)
+  float* stat_c = stat_il + GP;                                  // [GP] team: e_split -> p factor
+  uint64_t* best_w = reinterpret_cast<uint64_t*>(stat_c + GP);   // [NW]
   int* red_i = reinterpret_cast<int*>(best_w + NW);              // [NW]
   int* red_f = red_i + NW;                                       // [NW] fill step
   int* last = red_f + NW;                                        // team: last to finish the pair
-  static_assert(NW * GP * 4 + GP * 8 + NW * 8 + NW * 8 + 4 <= kTicketSlot,
+  static_assert(NW * GP * 4 + GP * 12 + NW * 8 + NW * 8 + 4 <= kTicketSlot,
                 "the reductions must stay below the team ticket in the scratch area");
 
   const size_t row0 = (size_t)pair * p.S;  // first cache row of this pair
@@ -364,6 +411,8 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   // the last valid row, so trailing masked rows are never streamed.  A fill
   // step also counts the slot it wrote as valid (whatever the mask byte
   // reads while other workgroups update it) and finds the lowest free slot.
+  int* kq = reinterpret_cast<int*>(smem + L.scratch + kBatchSlot);  // next phase-K batch
+  if (tid == 0) *kq = 0;
   int last_valid = -1;
   int first_free = INT_MAX;
   const int own = (p.fill && prev >= s0 && prev < s0 + n) ? prev - s0 : -1;
@@ -408,15 +457,26 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   float mx[HPL];
 #pragma unroll
   for (int i = 0; i < HPL; ++i) mx[i] = kNegInf;
-  // Batches of this wave, visited from a per-workgroup starting batch so
-  // that workgroups streaming at the same pace read addresses that differ
-  // by more than the power-of-two spacing of their cache rows.
-  const int nbatch = wave * ROWS < n_eff ? (n_eff - wave * ROWS + stride - 1) / stride : 0;
-  const int rot = MODE != kModeSingle && nbatch > 0 ? (int)(((unsigned)item * kRotate) % (unsigned)nbatch) : 0;
-  for (int bi = 0; bi < nbatch; ++bi) {
-    const int r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
+  // Phase K takes batches of ROWS rows in the order the waves ask for them
+  // (an LDS counter), so the waves of a workgroup finish it together (with
+  // a fixed share each, the last wave of a 16-wave team split finished
+  // 12 us after the first); each logit lands in its row's LDS word and the
+  // maximum does not depend on the order.  The split and team modes start
+  // from a per-workgroup batch, so that workgroups streaming at the same
+  // pace read addresses that differ by more than the power-of-two spacing
+  // of their cache rows.
+  const int nbk = (n_eff + ROWS - 1) / ROWS;
+  const int rotk = MODE != kModeSingle && nbk > 0 ? (int)(((unsigned)item * kRotate) % (unsigned)nbk) : 0;
+  int next = 0;
+  if (lane == 0) next = atomicAdd(kq, 1);
+  next = __builtin_amdgcn_readfirstlane(next);
+  while (next < nbk) {
+    const int bk = next + rotk < nbk ? next + rotk : next + rotk - nbk;
+    const int r0 = bk * ROWS;
     uint4 buf[U];
     const uint32_t ok = load_batch<D, U, RPW>(buf, krs, mk, r0, rg, c);
+    int claim = 0;
+    if (lane == 0) claim = atomicAdd(kq, 1);
     float* lrow = lg + (r0 + rg) * GP + hbase;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -433,7 +493,13 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
       }
       LF_ROW_FENCE();
     }
+    next = __builtin_amdgcn_readfirstlane(claim);
   }
+  // Phase V keeps a fixed share of rows per wave (rows wave * ROWS + k *
+  // stride), so each lane's O accumulators sum the same rows in the same
+  // order every time and O is the same bit for bit from run to run.
+  const int nbatch = wave * ROWS < n_eff ? (n_eff - wave * ROWS + stride - 1) / stride : 0;
+  const int rot = MODE != kModeSingle && nbatch > 0 ? (int)(((unsigned)item * kRotate) % (unsigned)nbatch) : 0;
 
   // ---- softmax statistics of this split
   // Lanes with equal c hold the same heads; fold the row groups, then waves.
@@ -462,17 +528,15 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     float lsum = 0.f;
     float* wl = SPLIT ? p.ws_logit + (row0 + s0) * GP : nullptr;
     // Rows up to the end of the last batch (all written in phase K, -inf
-    // when invalid) become e; invalid ones become exactly 0, so phase V
-    // needs no per-row select.
-    // A team member keeps its logits until the pair's max is known: here it
-    // only sums exp2 against its own max.
+    // when invalid) become e = exp2(s - split max); invalid ones become
+    // exactly 0, so phase V needs no per-row select.
     const int covered = (n_eff + ROWS - 1) / ROWS * ROWS;
     for (int r = tid / GP; r < covered; r += kThreads / GP) {
       const float s = lg[r * GP + h];
       const float e = (s == kNegInf) ? 0.f : exp2f(s - mh);
-      if (!TEAM) lg[r * GP + h] = e;
+      lg[r * GP + h] = e;
       lsum += e;
-      if (SPLIT && r < n_eff) wl[r * GP + h] = s;
+      if (SPLIT && r < n_eff) wl[r * GP + h] = e;
     }
 #pragma unroll
     for (int m = GP; m < 64; m <<= 1) lsum += __shfl_xor(lsum, m);
@@ -483,44 +547,22 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
       float l = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) l += red[w * GP + tid];
-      if (TEAM) {
-        // Publish this split's (max, sum), then rebuild the pair's as the
-        // combine kernel does: max over the splits, then the rescaled sums
-        // in split order (a split without a finite logit adds its sum as it
-        // is: 0 when it has no valid slot, NaN when its logits are NaN).
-        uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2;
-        team_publish(xs + (sp * GP + tid) * 2, stat_m[tid]);
-        team_publish(xs + (sp * GP + tid) * 2 + 1, l);
-        const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kTeamWaitTicks;
-        float gm = kNegInf;
-        for (int q = 0; q < nsplit; ++q) gm = fmaxf(gm, team_wait(xs + (q * GP + tid) * 2, p.status, deadline));
-        float gl = 0.f;
-        for (int q = 0; q < nsplit; ++q) {
-          const float mq = team_wait(xs + (q * GP + tid) * 2, p.status, deadline);
-          const float lq = team_wait(xs + (q * GP + tid) * 2 + 1, p.status, deadline);
-          gl += mq != kNegInf ? lq * exp2f(mq - gm) : lq;
-        }
-        stat_m[tid] = gm;
-        l = gl;
-      }
       stat_il[tid] = (l > 0.f || l != l) ? 1.0f / l : 0.f;  // NaN logits make every p NaN
       if (SPLIT) {
         float* ml = p.part_ml + (((size_t)pair * nsplit + sp) * GP + tid) * 2;
         ml[0] = stat_m[tid];
         ml[1] = l;
       }
+      if (TEAM) {
+        // Publish this split's (max, sum) and go on to phase V at once; the
+        // pair's statistics are read after it, when every split of the
+        // team has long passed this point.
+        uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2;
+        team_publish(xs + (sp * GP + tid) * 2, stat_m[tid]);
+        team_publish(xs + (sp * GP + tid) * 2 + 1, l);
+      }
     }
     __syncthreads();
-    if (TEAM) {
-      // e against the pair's max, the same expression as with one split, so
-      // equal K/V rows get equal scores whichever split holds them.
-      const float gmh = stat_m[h];
-      for (int r = tid / GP; r < covered; r += kThreads / GP) {
-        const float s = lg[r * GP + h];
-        lg[r * GP + h] = (s == kNegInf) ? 0.f : exp2f(s - gmh);
-      }
-      __syncthreads();
-    }
   }
 
   // ---- phase V: O accumulators, |v|_1, and (single split) scores
@@ -534,13 +576,17 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     for (int k = 0; k < 8; ++k) acc[h][k] = 0.f;
   uint64_t best = kNoCandidate;
 
-  // Each row's score (single split) or |v|_1 (several splits) goes into the
+  // Each row's score (single split) or |v|_1 (combine path) goes into the
   // LDS word that held the row's first logit, written by all lanes of the row
-  // group (same value), and leaves for HBM in one coalesced pass afterwards.
+  // group (same value), and leaves for HBM in one coalesced pass afterwards;
+  // a team split keeps |v|_1 in its own row of LDS for the scores it forms
+  // once the pair's statistics are known.
   auto finish_row = [&](float* slot, float vn, const float (&e)[GP], bool valid, int r) {
     vn = allreduce_sum<LPR / 2>(vn);
     if (SPLIT) {
       *slot = vn;
+    } else if (TEAM) {
+      vnl[r] = vn;
     } else {
       float ps = 0.f;
 #pragma unroll
@@ -578,7 +624,48 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     }
   }
   __syncthreads();
-  {
+  if constexpr (TEAM) {
+    // The pair's statistics, rebuilt as the combine kernel does: max over
+    // the splits, then the rescaled sums in split order (a split without a
+    // finite logit adds its sum as it is: 0 when it has no valid slot, NaN
+    // when its logits are NaN).  c turns this split's e into probabilities:
+    // p = e * exp2(split max - pair max) / L.
+    if (tid < GP) {
+      const uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2;
+      const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kTeamWaitTicks;
+      float gm = kNegInf;
+      for (int q = 0; q < nsplit; ++q) gm = fmaxf(gm, team_wait(xs + (q * GP + tid) * 2, p.status, deadline));
+      float gl = 0.f;
+      for (int q = 0; q < nsplit; ++q) {
+        const float mq = team_wait(xs + (q * GP + tid) * 2, p.status, deadline);
+        const float lq = team_wait(xs + (q * GP + tid) * 2 + 1, p.status, deadline);
+        gl = mq != kNegInf ? fmaf(lq, exp2f(mq - gm), gl) : gl + lq;
+      }
+      const float gil = (gl > 0.f || gl != gl) ? 1.0f / gl : 0.f;
+      const float ms = stat_m[tid];
+      stat_c[tid] = ms != kNegInf ? exp2f(ms - gm) * gil : 0.f;
+      stat_m[tid] = gm;
+      stat_il[tid] = gil;
+    }
+    __syncthreads();
+    // Scores of the split's rows, written in one coalesced pass, and the
+    // split's lowest (score, slot).
+    float cc[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) cc[h] = h < p.G ? stat_c[h] : 0.f;
+    for (int r = tid; r < n; r += kThreads) {
+      float sc = kInf;
+      if (r < n_eff && mk[r] != 0) {
+        float ps = 0.f;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) ps = fmaf(lg[r * GP + h], cc[h], ps);
+        sc = vnl[r] * ps;
+        const uint64_t cand = pack_candidate(sc, s0 + r);
+        best = cand < best ? cand : best;
+      }
+      p.scores[row0 + s0 + r] = sc;
+    }
+  } else {
     // Rows at or past n_eff are all masked: score +inf, no |v|_1 needed.
     float* dst = SPLIT ? p.ws_vnorm + row0 + s0 : p.scores + row0 + s0;
     const int lim = SPLIT ? n_eff : n;
@@ -586,23 +673,22 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   }
 
   // ---- O: fold the row groups of each wave, then the waves through LDS
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int m = LPR; m < 64; m <<= 1) acc[h][k] += __shfl_xor(acc[h][k], m);
+  static_assert(LPR == 16 || LPR == 8, "row groups of 16 or 8 lanes");
+  fold_row_groups<LPR, GP>(acc, lane);
   if (!SPLIT) {
     best = wave_min_u64(best);
     if (lane == 0) best_w[wave] = best;
   }
   __syncthreads();  // the logits region is reused below
   float* ored = lg;  // [NW][GP][D]
-  if (rg == 0) {
+  {
+    constexpr int PER = GP * 8 / (64 / LPR);  // sums each lane holds
+    const int fb = fold_base<LPR, GP>(lane);
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ored[(wave * GP + h) * D + c * 8 + k] = acc[h][k];
+    for (int i = 0; i < PER; ++i) {
+      const int g = fb + i;
+      ored[(wave * GP + g / 8) * D + c * 8 + (g & 7)] = acc[i / 8][i % 8];
+    }
   }
   __syncthreads();
 
@@ -668,13 +754,23 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     if (tid == 0) *last = atomicAdd(p.xcnt + pair, 1u) == (unsigned)(nsplit - 1);
     __syncthreads();
     if (*last) {
+      // O = sum over the splits of acc * exp2(split max - pair max), in split
+      // order, divided by L: the combine kernel's expression.
       const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kTeamWaitTicks;
       const uint64_t* xa = p.xo + (size_t)pair * nsplit * GP * D;
+      const uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2;
       for (int idx = tid; idx < GP * D; idx += kThreads) {
         const int h = idx / D;
         if (h >= p.G) continue;
+        const float gm = stat_m[h];
         float o = 0.f;
-        for (int q = 0; q < nsplit; ++q) o += team_wait(xa + (size_t)q * GP * D + idx, p.status, deadline);
+        if (gm != kNegInf) {
+          for (int q = 0; q < nsplit; ++q) {
+            const float mq = team_wait(xs + (q * GP + h) * 2, p.status, deadline);
+            const float pv = team_wait(xa + (size_t)q * GP * D + idx, p.status, deadline);
+            if (mq != kNegInf) o = fmaf(pv, exp2f(mq - gm), o);
+          }
+        }
         p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] = f32_to_bf16_rne(o * stat_il[h]);
       }
       if (tid == 0) {
@@ -713,7 +809,7 @@ __device__ __forceinline__ DecodeParams reload_params() {
 template <int D, int GP, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int* tk = reinterpret_cast<int*>(smem + lds_layout(D, GP, p.split_len, NW).scratch + kTicketSlot);
+  int* tk = reinterpret_cast<int*>(smem + lds_layout(D, GP, p.split_len, NW, MODE == kModeTeam).scratch + kTicketSlot);
   if constexpr (MODE == kModeSingle) {
     // Persistent workgroups: workgroup w takes pair w first, then further
     // pairs from the work-item counter (tickets gridDim.x, gridDim.x + 1, ...)
@@ -795,11 +891,14 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
 //
 // After a split decode.  longflow_combine_kernel: one workgroup per (pair,
 // chunk of kCombineRows slots).  It rebuilds the pair's global max M_h and sum
-// L_h from the split partials, writes score_i = |v_i|_1 * sum_h exp2(s_hi -
-// M_h) / L_h for the valid slots of its chunk (+inf elsewhere) and the
-// chunk's lowest-index minimum; chunk 0 also writes O = sum_s acc_s *
-// exp2(m_s - M_h) / L_h.  longflow_finalize_kernel then takes the minimum
-// over the chunks of each pair.
+// L_h from the split partials, and for every split q the factor c_qh =
+// exp2(m_qh - M_h) / L_h that turns the split's e = exp2(s - m_qh) into
+// probabilities.  It writes score_i = |v_i|_1 * sum_h e_hi c_qh for the valid
+// slots of its chunk (+inf elsewhere) and the chunk's lowest-index minimum;
+// chunk 0 also writes O = sum_q acc_q exp2(m_q - M_h) / L_h.
+// longflow_finalize_kernel then takes the minimum over the chunks of each
+// pair.  The team path forms its scores and O with the same expressions in
+// the same order, so the two paths give the same scores bit for bit.
 
 constexpr int kCombineThreads = 256;
 constexpr int kCombineRowsPerThread = 8;
@@ -811,6 +910,7 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
   constexpr int NWC = kCombineThreads / 64;
   constexpr int R = kCombineRowsPerThread;
   __shared__ float stat_m[GP], stat_il[GP];
+  __shared__ float cs[kMaxSplits * GP];  // [split][head] e -> p factors
   __shared__ uint64_t best_w[NWC];
   __shared__ int free_w[NWC];
 
@@ -830,9 +930,9 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
   const uint8_t* mrow = p.mask + (size_t)b * p.S;
   float* sr = p.scores + row0;
   const int base = chunk * kCombineRows;
-  // Every load is issued, mask, logits and |v|_1 together, before any is
-  // used (rows past S read row S - 1); the mask only decides what the values
-  // are used for.  A masked row's workspace entry may be stale and is never
+  // Every load is issued, mask, e and |v|_1 together, before any is used
+  // (rows past S read row S - 1); the mask only decides what the values are
+  // used for.  A masked row's workspace entry may be stale and is never
   // used.
   bool valid[R];
   uint8_t mk[R];
@@ -883,10 +983,18 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
       }
 #pragma unroll
       for (int u = 0; u < SB; ++u)
-        if (s0 + u < nsplit) l += ms[u] != kNegInf ? ls[u] * exp2f(ms[u] - m) : ls[u];
+        if (s0 + u < nsplit) l = ms[u] != kNegInf ? fmaf(ls[u], exp2f(ms[u] - m), l) : l + ls[u];
     }
     stat_m[tid] = m;
     stat_il[tid] = (l > 0.f || l != l) ? 1.0f / l : 0.f;
+  }
+  __syncthreads();
+  // e -> p factor of every (split, head); zero for padded heads.
+  for (int i = tid; i < nsplit * GP; i += kCombineThreads) {
+    const int q = i / GP, h = i - q * GP;
+    const float mq = ml[(q * GP + h) * 2];
+    const float gil = h < p.G ? stat_il[h] : 0.f;
+    cs[i] = mq != kNegInf ? exp2f(mq - stat_m[h]) * gil : 0.f;
   }
   __syncthreads();
 
@@ -909,7 +1017,7 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
           }
 #pragma unroll
           for (int u = 0; u < SB; ++u)
-            if (s0 + u < nsplit && ms[u] != kNegInf) o += pv[u] * exp2f(ms[u] - m);
+            if (s0 + u < nsplit && ms[u] != kNegInf) o = fmaf(pv[u], exp2f(ms[u] - m), o);
         }
       }
       p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] =
@@ -917,12 +1025,6 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
     }
   }
 
-  float gm[GP], gil[GP];
-#pragma unroll
-  for (int h = 0; h < GP; ++h) {
-    gm[h] = stat_m[h];
-    gil[h] = h < p.G ? stat_il[h] : 0.f;
-  }
 #pragma unroll
   for (int u = 0; u < R; ++u) valid[u] = base + u * kCombineThreads + tid < p.S && mk[u] != 0;
   // Fill step: the lowest free slot of the chunk.  The decode kernel has
@@ -944,9 +1046,10 @@ __global__ __launch_bounds__(kCombineThreads) void longflow_combine_kernel(Decod
     const int r = base + u * kCombineThreads + tid;
     float sc = kInf;
     if (valid[u]) {
+      const float* cq = cs + (r / p.split_len) * GP;
       float ps = 0.f;
 #pragma unroll
-      for (int h = 0; h < GP; ++h) ps = fmaf(exp2f(s[u][h] - gm[h]), gil[h], ps);
+      for (int h = 0; h < GP; ++h) ps = fmaf(s[u][h], cq[h], ps);
       sc = vn[u] * ps;
       const uint64_t cand = pack_candidate(sc, r);
       best = cand < best ? cand : best;

@@ -210,14 +210,21 @@ def test_checkpoint_resume_is_bitwise():
     assert torch.equal(a.dk.view(torch.int16), c.dk.view(torch.int16))
 
 
-def test_twins_tie_to_lowest_index():
-    """Exact duplicate K/V rows get bit-identical scores; the lower slot wins."""
+@pytest.mark.parametrize("other", [450, 250], ids=["other_split", "same_split"])
+def test_twins_tie_to_lowest_index(other):
+    """Exact duplicate K/V rows (slots 120 and `other`, the smallest score
+    of the row) get bit-identical scores whenever one workgroup scores both:
+    with one split, and with several when both fall in one split; the lower
+    slot wins.  In different splits each score carries its split's own
+    exp2(split max - pair max) factor, so the two may differ in the last
+    bits; the evicted slot is then one of the twins (a near-tie of the
+    acceptance rule) and holds the minimum of the GPU's own scores."""
     from decode_attention_kv_05_amd import longflow as lf
     wl = W.Workload("twins", B=1, Hq=4, Hkv=1, d=128, S=600, steps=1, seed=46)
     k, v, mask = W.initial_cache(wl)
-    v[0, 0, 450] = (v[0, 0, 450].astype(np.uint32) & 0x8000 | 0x2000).astype(np.uint16)  # tiny |v|
-    k[0, 0, 120] = k[0, 0, 450]
-    v[0, 0, 120] = v[0, 0, 450]
+    v[0, 0, other] = (v[0, 0, other].astype(np.uint32) & 0x8000 | 0x2000).astype(np.uint16)  # tiny |v|
+    k[0, 0, 120] = k[0, 0, other]
+    v[0, 0, 120] = v[0, 0, other]
     q, nk, nv = W.step_inputs(wl, 0)
     for nsplit, path in split_variants((1, 2, 4)):
         out, sc, ev = lf.longflow_decode(bf16_dev(q), bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda(),
@@ -226,8 +233,13 @@ def test_twins_tie_to_lowest_index():
                                          split_path=path)
         torch.cuda.synchronize()
         s = sc.cpu().numpy()
-        assert s[0, 0, 120] == s[0, 0, 450]
-        assert ev.item() == 120, (nsplit, ev.item())
+        split_len = -(-600 // nsplit)
+        if 120 // split_len == other // split_len:
+            assert s[0, 0, 120] == s[0, 0, other], (nsplit, path)
+            assert ev.item() == 120, (nsplit, path, ev.item())
+        else:
+            assert abs(float(s[0, 0, 120]) - float(s[0, 0, other])) <= 1e-6 * float(s[0, 0, other]), (nsplit, path)
+            assert ev.item() in (120, other), (nsplit, path, ev.item())
         global_properties(sc, ev, torch.from_numpy(mask).cuda())
 
 
