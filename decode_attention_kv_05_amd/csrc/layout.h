@@ -159,9 +159,11 @@ constexpr size_t kScratchBytes = 1024;
 // the bytes below them.
 constexpr size_t kTicketSlot = kScratchBytes - 16;
 constexpr size_t kBatchSlot = kScratchBytes - 12;
-// Rows past the end of a split that a wave batch may touch; the mask and
-// logit arrays are padded by this much so those reads need no bounds check.
-constexpr int kRowPad = 128;
+// Rows past the end of a split that a wave batch may touch (a batch is 16
+// rows at d = 128, 32 at d = 64, and the last one may run past the split by
+// all but one of its rows); the mask and logit arrays are padded by this
+// much so those accesses need no bounds check.
+constexpr int kRowPad = 32;
 
 // LDS a workgroup may use so that two of them share a compute unit.
 constexpr size_t kHalfLdsBytes = 80 * 1024;
