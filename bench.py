@@ -238,7 +238,7 @@ def cpu_baseline_fill(wl, max_pairs, fill_from, min_seconds=10.0):
     }
 
 
-def timed(step, K, Wm, stream, dev, reset=None):
+def timed(step, K, Wm, stream, dev, reset=None, warmup_s=WARMUP_MIN_S):
     """Warm up with at least Wm steps and at least WARMUP_MIN_S seconds of
     them; then REPEATS times: K steps between one pair of events on the
     launch stream, synchronized on both sides.  Then K steps, untimed as a
@@ -252,7 +252,7 @@ def timed(step, K, Wm, stream, dev, reset=None):
     import torch
     t = 0
     w0 = time.perf_counter()
-    while t < Wm or time.perf_counter() - w0 < WARMUP_MIN_S:
+    while t < Wm or time.perf_counter() - w0 < warmup_s:
         for _ in range(max(1, Wm)):
             step(t)
             t += 1
@@ -381,6 +381,8 @@ def main():
     ap.add_argument("--hidden", type=int, default=4096, help="model width in stack mode")
     ap.add_argument("--topk-k", type=int, default=128, help="slots chosen per pair in topk mode")
     ap.add_argument("--cadence", type=int, default=128, help="steps between top-k refreshes in cadence mode")
+    ap.add_argument("--warmup-seconds", type=float, default=WARMUP_MIN_S,
+                    help="the warm-up lasts at least this long (counter runs under a profiler pass 0)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times "
                          "(calibrates HBM byte counters) and exit")
@@ -484,7 +486,7 @@ def main():
             dm.copy_(dm0)
             slots[t % 2].fill_(fill_from if fill_from < wl.S else -1)
 
-    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev, reset)
+    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev, reset, args.warmup_seconds)
     ms_per_step = float(np.median(reps))
     status = lf.lf_read_device_status(ws)
     if status:
@@ -540,7 +542,7 @@ def main():
         "roofline": rl,
         "timing": {"repeats": REPEATS, "steps_per_repeat": K, "statistic": "median",
                    "ms_per_step_repeats": [round(float(x), 5) for x in reps],
-                   "warmup_steps_run": warm, "warmup_min_s": WARMUP_MIN_S},
+                   "warmup_steps_run": warm, "warmup_min_s": args.warmup_seconds},
         "wall_s_timed": round(wall, 3),
     }
     result["hbm_probe"] = hbm_probes(dev, dk, dv)
@@ -574,7 +576,7 @@ def bench_topk(args, wl, lf, W, dev):
     def step(t):
         lf.longflow_evict_topk(scores, mask, k, out=out, stream=stream)
 
-    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev)
+    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev, warmup_s=args.warmup_seconds)
     ms = float(np.median(reps))
     algb = topk_bytes(B, Hkv, S, k)
     result = {
@@ -678,7 +680,7 @@ def bench_stack(args, wl, lf, W, dev):
         x_in.copy_(xs[t % n_inputs], non_blocking=True)
         graph.launch(stream)
 
-    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev)
+    reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev, warmup_s=args.warmup_seconds)
     ms = float(np.median(reps))
     status = lf.lf_read_device_status(stack.tensors["workspace"])
     graph.close()
