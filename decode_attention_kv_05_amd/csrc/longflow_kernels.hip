@@ -44,9 +44,12 @@
 // decides exact ties.
 
 #include <hip/hip_runtime.h>
+
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "launch.h"
 #include "layout.h"
@@ -186,8 +189,11 @@ __device__ __forceinline__ void fold_row_groups(float (&a)[GP][8], int lane) {
 #pragma unroll
     for (int i = 0; i < N / 8; ++i) {
       const int j = N / 8 + i;
-      const float send = upper ? a[i / 8][i % 8] : a[j / 8][j % 8];
-      const float keep = upper ? a[j / 8][j % 8] : a[i / 8][i % 8];
+      // select values, not array elements: a select of two element
+      // addresses keeps the compiler from holding the array in registers
+      const float lo = a[i / 8][i % 8], hi = a[j / 8][j % 8];
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
       a[i / 8][i % 8] = keep + partner<8>(send);
     }
   }
@@ -1161,12 +1167,43 @@ hipError_t occupancy_d(bool team, int gp, int nw, size_t lds, int* blocks) {
   }
 }
 
-hipError_t decode_blocks_per_cu(bool team, int d, int gp, int nw, size_t lds, int* blocks) {
+static hipError_t query_blocks_per_cu(bool team, int d, int gp, int nw, size_t lds, int* blocks) {
   switch (d) {
     case 64: return occupancy_d<64>(team, gp, nw, lds, blocks);
     case 128: return occupancy_d<128>(team, gp, nw, lds, blocks);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The occupancy query costs several microseconds of host time, as much as a
+// small step's whole launch, and its answer depends only on the device and
+// the kernel configuration: answers are kept per (device, configuration).
+hipError_t decode_blocks_per_cu(bool team, int d, int gp, int nw, size_t lds, int* blocks) {
+  struct Entry {
+    int dev, team, d, gp, nw, blocks;
+    size_t lds;
+  };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i) {
+      const Entry& c = cache[i];
+      if (c.dev == dev && c.team == (int)team && c.d == d && c.gp == gp && c.nw == nw && c.lds == lds) {
+        *blocks = c.blocks;
+        return hipSuccess;
+      }
+    }
+  }
+  e = query_blocks_per_cu(team, d, gp, nw, lds, blocks);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 64) cache[used++] = Entry{dev, (int)team, d, gp, nw, *blocks, lds};
+  return hipSuccess;
 }
 
 template <int D>
