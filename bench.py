@@ -19,9 +19,10 @@ probes on the same GPU give the box's practical HBM rates.  Prints one JSON
 line.
 
 Other modes measure the cache-lifecycle entry points on the same shape:
-  fill     longflow_decode_fill on caches that start 2K + W slots short of
-           full and reach full at the last step (the mask grows by one slot
-           per sequence and step)
+  fill     longflow_decode_fill: every timed pass starts from caches K slots
+           short of full (the mask and the first slot restored before each
+           pass) and reaches full at its last step (the mask grows by one
+           slot per sequence and step)
   topk     longflow_evict_topk choosing --topk-k slots from synthetic scores
   cadence  longflow_decode with the written slots taken from a top-k queue
            refreshed every --cadence steps (periodic compression)
