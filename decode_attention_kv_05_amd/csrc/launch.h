@@ -19,7 +19,7 @@ struct DecodeParams {
   float* scores;          // [B][Hkv][S]
   int32_t* evict;         // [B][Hkv]
   uint32_t* status;       // workspace: LF_DEV_* bits
-  uint32_t* queue;        // workspace: [2] single-split work-item counter, finished workgroups
+  uint32_t* queue;        // workspace: [3] single-split work-item counter, finished workgroups; team claims
   float* part_ml;         // workspace: [pairs][nsplit][GP][2]
   float* part_o;          // workspace: [pairs][nsplit][GP][d]
   float* ws_logit;        // workspace: [pairs][S][GP]
@@ -32,7 +32,6 @@ struct DecodeParams {
   uint64_t* xo;           // team: [pairs][nsplit][GP][d] published O accumulators
   uint32_t* xcnt;         // team: [pairs] splits finished
   uint32_t* xticket;      // team: [kTicketRanges] work items handed out per range
-  size_t team_words;      // team: 32-bit words of the region above, zeroed before the launch
   int pairs;              // B * Hkv
   int Hq, Hkv, G, S, nsplit, split_len;
   int fill;               // 1: fill step (next slot = lowest free slot while any)

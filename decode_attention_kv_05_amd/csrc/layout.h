@@ -56,8 +56,9 @@ LF_HD inline void split_geometry(int S, int nsplit, int* split_len, int* nsplit_
 // Byte offsets inside the caller's workspace.
 struct WorkspaceLayout {
   size_t status;    // uint32: LF_DEV_* bits
-  size_t queue;     // uint32 [2]: single-split work-item counter and finished-workgroup
-                    // count; zero between launches (each launch's last workgroup resets them)
+  size_t queue;     // uint32 [3]: single-split work-item counter and finished-workgroup
+                    // count, team launch's claimed-workgroup count; zero between
+                    // launches (each launch's last workgroup resets them)
   size_t part_ml;   // float [pairs][nsplit][GP][2]: split max and sum of exp2
   size_t part_o;    // float [pairs][nsplit][GP][d]: split output accumulators
   size_t logit;     // float [pairs][S][GP]: log2-domain logits

@@ -302,7 +302,6 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
     prm.xo = reinterpret_cast<uint64_t*>(ws + tl.xo);
     prm.xcnt = reinterpret_cast<uint32_t*>(ws + tl.xcnt);
     prm.xticket = reinterpret_cast<uint32_t*>(ws + tl.xticket);
-    prm.team_words = tl.zero_words;
   }
   // One split: as many persistent workgroups as the device holds at once
   // (fewer when there are fewer pairs); they take the pairs from the

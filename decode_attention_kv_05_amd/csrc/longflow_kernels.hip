@@ -794,6 +794,20 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
         if (p.fill && ff != (uint32_t)INT_MAX) next = (int32_t)ff;
         p.evict[pair] = next;
       }
+      // Leave the pair's words at zero for the next step.  Every split has
+      // read all it needs from them: each reads the statistics before it
+      // publishes and counts itself in, and this last split has read the rest.
+      __syncthreads();
+      uint64_t* zo = p.xo + (size_t)pair * nsplit * GP * D;
+      for (int i = tid; i < nsplit * GP * D; i += kThreads)
+        __hip_atomic_store(zo + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint64_t* zs = p.xstat + (size_t)pair * nsplit * GP * 2;
+      for (int i = tid; i < nsplit * GP * 2; i += kThreads)
+        __hip_atomic_store(zs + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint64_t* zf = p.xfin + (size_t)pair * nsplit * 3;
+      for (int i = tid; i < nsplit * 3; i += kThreads)
+        __hip_atomic_store(zf + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(p.xcnt + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -853,7 +867,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
   } else if constexpr (MODE == kModeTeam) {
     // Work items go out by tickets in the order workgroups start, not by
     // block index.  The pairs form kTicketRanges ranges of whole teams, each
-    // with its own counter (zeroed with the exchange words); a workgroup
+    // with its own counter (left at zero by the previous launch); a workgroup
     // claims from range (block index mod kTicketRanges) first and from the
     // next ranges once that one is used up.  There are as many workgroups as
     // items, so every claim succeeds.  Within a range tickets go out in start
@@ -876,6 +890,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
         if (t < (unsigned)(hi - lo)) claimed = lo + (int)t;
       }
       *tk = claimed;
+      // Every workgroup has made its last claim once all have counted
+      // themselves in here (each counts after its claims have returned): the
+      // last one zeroes the ticket counters and this count for the next launch.
+      if (atomicAdd(p.queue + 2, 1u) == gridDim.x - 1) {
+        for (int r = 0; r < kTicketRanges; ++r) atomicExch(p.xticket + r, 0u);
+        atomicExch(p.queue + 2, 0u);
+      }
     }
     __syncthreads();
     const int t = *tk;
@@ -1105,9 +1126,9 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
 template <int D, int GP, int NW>
 hipError_t launch_dgw(const DecodeParams& prm, int nblocks, size_t lds, int team_grid, int grid, hipStream_t stream) {
   if (team_grid > 0) {
-    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(prm.xstat), prm.team_words, 0u, stream);
-    if (e != hipSuccess) return e;
-    // One plain launch of every (pair, split): the ticket order (see the
+    // The exchange region is all zero: from the workspace's first zero fill,
+    // and after every team launch (each team zeroes its words and the last
+    // workgroup the counters).  One plain launch of every (pair, split): the ticket order (see the
     // kernel) needs no co-residency promise, so no cooperative launch (which
     // cost 11-19 us more per launch) and no rounds.
     hipLaunchKernelGGL((longflow_decode_kernel<D, GP, NW, kModeTeam>), dim3(team_grid), dim3(NW * 64), lds,

@@ -56,9 +56,11 @@
  * one stream.
  *
  * Workspace: zero-filled before its first use (lf_workspace_init, or any
- * zeroing of the memory).  It holds the device status word and the work-item
- * counters of the one-split step, which every call leaves at zero for the
- * next; everything else in it is scratch for the duration of a call.
+ * zeroing of the memory).  It holds the device status word, the work-item
+ * counters of the one-split step and the team path's exchange words, which
+ * every completed call leaves at zero for the next; everything else in it is
+ * scratch for the duration of a call.  After a step that reports
+ * LF_DEV_TEAM_TIMEOUT, zero it again before its next use.
  *
  * Errors: every entry point returns LF_OK (0) or a negative lf_status code
  * from host-side checks made before anything is enqueued; nothing is enqueued
@@ -103,7 +105,8 @@ typedef enum lf_status {
                                      the other splits of its pair, which happens only
                                      when they were kept from running (another
                                      process holding compute units); that step's
-                                     results are unspecified */
+                                     results are unspecified, and the workspace
+                                     must be zeroed before its next use */
 
 /* How a step with several slot splits per (b, j) pair is finished. */
 #define LF_SPLIT_AUTO 0    /* LF_SPLIT_TEAM for up to 64 splits when the device
@@ -113,8 +116,10 @@ typedef enum lf_status {
                               a finalize kernel rescale them to the true softmax */
 #define LF_SPLIT_TEAM 2    /* the splits of a pair run together as a team of
                               workgroups, exchange their (max, sum) through the
-                              workspace mid-step, and score their slots against
-                              the pair's softmax with the logits kept on chip;
+                              workspace, and score their slots against
+                              the pair's softmax with the logits kept on chip
+                              (the statistics are read after each split has
+                              streamed its whole slot range);
                               the last split of a pair to finish writes O and
                               the evicted slot.  Workgroups take (pair, split)
                               tickets in the order they start, so the step

@@ -282,8 +282,8 @@ def test_team_path_equals_combine_path(B, Hq, Hkv, S, nsplit):
 def test_team_path_replays_in_a_graph():
     """A team-path step captured in a HIP graph: five replays, each after new
     queries are copied in (eager work between the replays), equal bit for
-    bit to an eager call on the same inputs.  The fill kernel that clears the
-    exchange words is part of the graph, so every replay starts clean."""
+    bit to an eager call on the same inputs.  Every team launch leaves its
+    exchange words and counters at zero, so every replay starts clean."""
     from decode_attention_kv_05_amd import longflow as lf
     wl = W.Workload("graph_team", B=2, Hq=16, Hkv=2, d=128, S=4096, steps=6, kind="lognormal_v", seed=8300)
     k, v, mask = W.initial_cache(wl)
@@ -320,3 +320,34 @@ def test_team_path_replays_in_a_graph():
         assert torch.equal(og.view(torch.int16), oe.view(torch.int16))
         assert torch.equal(sg.view(torch.int32), se.view(torch.int32)) and torch.equal(eg, ee)
         assert lf.lf_read_device_status(ws_g) == 0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,nsplit,path", [
+    (2, 32, 8, 8192, 4, "team"), (3, 16, 4, 1500, 5, "team"), (16, 64, 8, 4096, 64, "team"),
+    (2, 32, 8, 8192, 4, "combine"), (512, 32, 8, 256, 1, None), (1, 4, 1, 256, 1, None)])
+def test_workspace_left_zero(B, Hq, Hkv, S, nsplit, path):
+    """Every completed step leaves the whole workspace at zero: the status
+    word (no flags), the persistent workgroups' counters (the 4096-pair case
+    has more pairs than workgroups, so they are used), the team path's
+    exchange words, arrival and ticket counters (the 64-split case has more
+    teams than the device holds at once) and, on team steps, the combine
+    path's untouched arrays; on combine steps, the header.  So the next step
+    needs no zero fill.  Three steps in a row."""
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("ws_zero", B=B, Hq=Hq, Hkv=Hkv, d=128, S=S, steps=3, kind="lognormal_v", seed=8400)
+    k, v, mask = W.initial_cache(wl)
+    dk, dv, dm = bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda()
+    ws = lf.new_workspace(B, Hq, Hkv, 128, S, nsplit)
+    prev = torch.full((B, Hkv), -1, dtype=torch.int32, device="cuda")
+    for t in range(3):
+        log(f"B={B} Hq={Hq} Hkv={Hkv} S={S} nsplit={nsplit} path={path} step {t}")
+        q, nk, nv = W.step_inputs(wl, t)
+        _, _, ev = lf.longflow_decode(bf16_dev(q), dk, dv, dm, bf16_dev(nk), bf16_dev(nv), prev,
+                                      scale=float(wl.scale), workspace=ws, nsplit=nsplit, split_path=path)
+        prev = ev
+        torch.cuda.synchronize()
+        # the combine path's arrays (past the header and the team region) are
+        # its scratch; check its header only
+        kept = ws[:256] if path == "combine" else ws
+        nz = torch.nonzero(kept).flatten()
+        assert nz.numel() == 0, f"step {t}: {nz.numel()} nonzero workspace bytes, first at {nz[:8].tolist()}"
