@@ -506,10 +506,12 @@ extern "C" int longflow_decode_noalloc(int B, int Hq, int Hkv, int d, int S, flo
   rc = validate_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, new_k, new_v, prev_slot, out, scores,
                      evict_slot, ws, (size_t)LF_STATIC_SCRATCH_BYTES, nsplit, false, team_only);
   if (rc != LF_OK) return rc;
-  // The previous call on this device left its status bits and counters
-  // here; this call starts from zero (a fill kernel, so the call can be
-  // recorded into a graph).
-  if (lf::launch_fill_u32(static_cast<uint32_t*>(ws), 64, 0u, static_cast<hipStream_t>(stream)) != hipSuccess)
+  // The previous call on this device left its status bits here, and, had
+  // one of its team waits run out, set exchange words: this call's header
+  // and team region start from zero (a fill kernel, so the call can be
+  // recorded into a graph; its caller cannot zero a workspace it never sees).
+  const size_t clear = team_only ? need : 256;
+  if (lf::launch_fill_u32(static_cast<uint32_t*>(ws), clear / 4, 0u, static_cast<hipStream_t>(stream)) != hipSuccess)
     return LF_E_HIP;
   return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, nullptr, new_k, new_v,
                                  prev_slot, out, scores, evict_slot, ws, nsplit, LF_SPLIT_AUTO, stream, team_only);

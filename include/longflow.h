@@ -274,7 +274,8 @@ int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags);
  * may not call hipMalloc, harnesses that forbid allocation.  Same operator,
  * arguments, shapes, plan and results as longflow_decode (the same kernels);
  * the workspace is the library's own LF_STATIC_SCRATCH_BYTES device array,
- * cleared (by a fill kernel on `stream`) at the start of every call.  The
+ * whose header (and, on the team path, exchange region) a fill kernel on
+ * `stream` clears at the start of every call.  The
  * call allocates nothing and makes no allocating library call; the array's
  * device address is looked up on the first call on each device.
  * A step that needs more scratch than the array holds returns LF_E_SCRATCH
