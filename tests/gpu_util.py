@@ -100,6 +100,23 @@ def oracle_every_pair(q, k, v, mask, nk, nv, prev, scale):
             np.concatenate([r[2] for r in res]))
 
 
+def oracle_fill_every_seq(q, k, v, mask, nk, nv, prev, scale):
+    """decode_step_fill over every sequence, one sequence per task on a
+    thread pool; returns (O, scores, next slot, updated mask) as one
+    decode_step_fill call over the whole batch would (the host arrays are
+    not modified)."""
+    from threadpoolctl import threadpool_limits
+    B = q.shape[0]
+
+    def one(b):
+        sl = slice(b, b + 1)
+        return decode_step_fill(q[sl], k[sl].copy(), v[sl].copy(), mask[sl].copy(), nk[sl], nv[sl], prev[sl], scale)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(oracle_workers()) as ex:
+        res = list(ex.map(one, range(B)))
+    return tuple(np.concatenate([r[i] for r in res]) for i in range(4))
+
+
 def fill_sentinels(out, scores, evict):
     """Outputs a step must overwrite: NaN O and scores, -2 slots, so that a
     pair the step leaves unwritten fails every later check."""

@@ -15,7 +15,8 @@ import pytest
 import torch
 
 from decode_attention_kv_05_amd import workloads as W
-from gpu_util import (TIE_RTOL, FillLockstep, bf16_dev, bf16_host, bf16_value, compare_pair, log, lowest_free,
+from gpu_util import (TIE_RTOL, FillLockstep, all_outputs_written, bf16_dev, bf16_host, bf16_value, compare_pair,
+                      fill_sentinels, log, lowest_free, oracle_fill_every_seq,
                       split_variants)
 from oracle import decode_step, decode_step_fill, evict_topk
 
@@ -220,12 +221,13 @@ def test_periodic_cadence(nsplit, path):
 
 # ---------------------------------------------------------------- full size
 
-@pytest.mark.parametrize("name,len_lo,sample", [("qwen3_8b", 3000, [0, 37, 101, 127]),
-                                                ("long_reasoning", 16000, [0, 9])])
-def test_fill_step_full_size(name, len_lo, sample):
+@pytest.mark.parametrize("name,len_lo", [("qwen3_8b", 3000), ("long_reasoning", 16000)])
+def test_fill_step_full_size(name, len_lo):
     """One fill step at full size (the device's split plan) with up to a few
-    hundred free slots per sequence; sampled sequences against the oracle,
-    the mask update everywhere."""
+    hundred free slots per sequence: every (sequence, KV head) pair against
+    the oracle (a thread pool over the host's cores), outputs preset to
+    sentinels so that an unwritten pair fails, and the mask update and every
+    free-slot choice exact."""
     lf = _lf()
     base = W.WORKLOADS[name]
     wl = base.replace(name=name + "_fill", kind="ragged", len_lo=len_lo)
@@ -235,10 +237,15 @@ def test_fill_step_full_size(name, len_lo, sample):
     q, nk, nv = W.step_inputs(wl, 0)
     dk, dv, dm = bf16_dev(k), bf16_dev(v), torch.from_numpy(mask).cuda()
     ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S)
-    out, sc, nx = lf.longflow_decode_fill(bf16_dev(q), dk, dv, dm, bf16_dev(nk), bf16_dev(nv),
-                                          torch.from_numpy(prev).cuda(), scale=float(wl.scale), workspace=ws)
+    out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device="cuda")
+    sc = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device="cuda")
+    nx = torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device="cuda")
+    fill_sentinels(out, sc, nx)
+    lf.longflow_decode_fill(bf16_dev(q), dk, dv, dm, bf16_dev(nk), bf16_dev(nv), torch.from_numpy(prev).cuda(),
+                            scale=float(wl.scale), out=out, scores=sc, next_slot=nx, workspace=ws)
     torch.cuda.synchronize()
     assert lf.lf_read_device_status(ws) == 0
+    all_outputs_written(out, sc, nx)
     want_mask = mask.copy()
     for b in range(wl.B):
         if prev[b, 0] >= 0:
@@ -248,17 +255,17 @@ def test_fill_step_full_size(name, len_lo, sample):
     want_next = lowest_free(want_mask)
     full = want_next < 0
     assert np.array_equal(n_gpu[~full], np.repeat(want_next[~full, None], wl.Hkv, axis=1))
+    log(f"  {wl.name}: oracle over all {wl.B} sequences")
+    o_ref, s_ref, n_ref, m_ref = oracle_fill_every_seq(q, k, v, mask, nk, nv, prev, wl.scale)
+    assert np.array_equal(m_ref, want_mask)
     o_gpu = bf16_value(bf16_host(out))
-    sb = np.array(sample)
-    o_ref, s_ref, n_ref, m_ref = decode_step_fill(q[sb], k[sb], v[sb], mask[sb], nk[sb], nv[sb], prev[sb],
-                                                  wl.scale)
-    for r, b in enumerate(sample):
-        s_gpu = sc[b].cpu().numpy().astype(np.float64)
+    s_all = sc.cpu().numpy().astype(np.float64)
+    for b in range(wl.B):
         for j in range(wl.Hkv):
             heads = slice(j * wl.G, (j + 1) * wl.G)
-            compare_pair(o_gpu[b, heads], s_gpu[j], n_gpu[b, j], o_ref[r, heads], s_ref[r, j], n_ref[r, j],
-                         m_ref[r] != 0, f"{wl.name} b={b} j={j}")
-    log(f"  {wl.name}: sequences {sample} match; mask and free-slot choices exact for all {wl.B}")
+            compare_pair(o_gpu[b, heads], s_all[b, j], n_gpu[b, j], o_ref[b, heads], s_ref[b, j], n_ref[b, j],
+                         m_ref[b] != 0, f"{wl.name} b={b} j={j}")
+    log(f"  {wl.name}: every pair matches; mask and free-slot choices exact")
 
 
 @pytest.mark.parametrize("path", ["team", "combine"])
