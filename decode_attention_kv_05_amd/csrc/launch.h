@@ -19,7 +19,8 @@ struct DecodeParams {
   float* scores;          // [B][Hkv][S]
   int32_t* evict;         // [B][Hkv]
   uint32_t* status;       // workspace: LF_DEV_* bits
-  uint32_t* queue;        // workspace: [3] single-split work-item counter, finished workgroups; team claims
+  uint32_t* queue;        // workspace: [3] single-split work-item counter, finished workgroups; team
+                          // claims; the schedule's words from word kSchedWord on
   float* part_ml;         // workspace: [pairs][nsplit][GP][2]
   float* part_o;          // workspace: [pairs][nsplit][GP][d]
   float* ws_logit;        // workspace: [pairs][S][GP]
@@ -32,6 +33,9 @@ struct DecodeParams {
   uint64_t* xo;           // team: [pairs][nsplit][GP][d] published O accumulators
   uint32_t* xcnt;         // team: [pairs] splits finished
   uint32_t* xticket;      // team: [kTicketRanges] work items handed out per range
+  uint32_t* lens;         // one split, longest-first schedule: [pairs] one past each pair's last
+                          // valid slot; null without the schedule
+  uint32_t* order;        // [2][kOrderMaxPairs] pair orders (one read, the other rebuilt)
   int pairs;              // B * Hkv
   int Hq, Hkv, G, S, nsplit, split_len;
   int fill;               // 1: fill step (next slot = lowest free slot while any)
@@ -45,8 +49,8 @@ struct TopkParams {
   int Hkv, S, k, pairs;
 };
 
-// team_grid > 0: after zeroing the team exchange words, one launch of the
-// team kernel with one workgroup per (pair, split), nblocks in all;
+// team_grid > 0: one launch of the team kernel with one workgroup per
+// (pair, split), nblocks in all;
 // otherwise, with one split, `grid` persistent workgroups of the
 // single-split kernel that take the nblocks pairs from the work-item counter,
 // or, with several, nblocks workgroups of the split kernel followed by the
@@ -64,11 +68,14 @@ hipError_t decode_blocks_per_cu(bool team, int d, int gp, int nw, size_t lds, in
 // written (by the same workgroup at its end, or by the finalize kernel).
 // team_only: the workspace holds only what a team-path step touches (a
 // split step then takes the team path or fails with LF_E_NSPLIT).
+// schedule: a one-split step keeps its longest-first pair order in the
+// workspace for the next step (off: pairs in index order, the schedule
+// region untouched).
 int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const void* q,
                         void* k_cache, void* v_cache, const uint8_t* mask, uint8_t* mask_w,
                         const void* new_k, const void* new_v, const int32_t* prev_slot, void* out,
                         float* scores, int32_t* evict_slot, void* workspace, int nsplit,
-                        int split_path, void* stream, bool team_only = false);
+                        int split_path, void* stream, bool team_only = false, bool schedule = true);
 hipError_t launch_topk(const TopkParams& prm, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 

@@ -53,12 +53,30 @@ LF_HD inline void split_geometry(int S, int nsplit, int* split_len, int* nsplit_
   *nsplit_eff = (S + len - 1) / len;
 }
 
+// Pairs of a one-split step that the persistent workgroups take longest
+// first; a step with more pairs takes them in index order.
+constexpr int kOrderMaxPairs = 4096;
+// Valid-extent words and the two pair-order buffers of that schedule.
+constexpr size_t kOrderRegionBytes = (size_t)3 * kOrderMaxPairs * 4;
+// The schedule's words, from queue word kSchedWord on (128 bytes into the
+// header, a cache line away from the counters every claim updates): [0]
+// the order buffer the next one-split step reads (0 or 1; each such step
+// flips it), [1 + buffer] the launch that buffer's order is for,
+// pairs << 16 | workgroups (0: none, or every pair alike).
+constexpr int kSchedWord = 28;
+
 // Byte offsets inside the caller's workspace.
 struct WorkspaceLayout {
   size_t status;    // uint32: LF_DEV_* bits
-  size_t queue;     // uint32 [3]: single-split work-item counter and finished-workgroup
-                    // count, team launch's claimed-workgroup count; zero between
-                    // launches (each launch's last workgroup resets them)
+  size_t queue;     // uint32 [3]: [0] single-split work-item counter, [1] finished-workgroup
+                    // count, [2] team launch's claimed-workgroup count (all zero
+                    // between launches: each launch's last workgroup resets them);
+                    // then, at word kSchedWord, the one-split schedule's words
+                    // (see kSchedWord)
+  size_t order;     // uint32 [3][kOrderMaxPairs]: one past the last valid slot of each
+                    // pair at its latest step, then two buffers of the pair indices
+                    // that the work-item counter hands out, longest first; written by
+                    // one-split steps only
   size_t part_ml;   // float [pairs][nsplit][GP][2]: split max and sum of exp2
   size_t part_o;    // float [pairs][nsplit][GP][d]: split output accumulators
   size_t logit;     // float [pairs][S][GP]: log2-domain logits
@@ -81,15 +99,19 @@ LF_HD inline size_t team_region_bytes(size_t pairs, int nsplit_eff, int gp, int 
 constexpr int kCombineSlots = 2048;
 LF_HD inline int combine_chunks(int S) { return (S + kCombineSlots - 1) / kCombineSlots; }
 
-// The status word and the work-item counters first, then (several splits)
-// the team exchange region, then the combine path's arrays: a team-path step
-// touches only the first team_workspace_bytes of the workspace.
+// The status word and the work-item counters first, then the one-split
+// schedule, then (several splits) the team exchange region and the combine
+// path's arrays: a team-path step touches only the first
+// team_workspace_bytes of the workspace.  The schedule region has the same
+// place and size for every shape, so what one-split steps leave there never
+// lies under another step's team words, whatever shapes share the workspace.
 LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int gp, int nsplit_eff) {
   WorkspaceLayout w{};
   const size_t pairs = (size_t)B * (size_t)Hkv;
-  size_t off = 256;
   w.status = 0;
   w.queue = 16;
+  w.order = 256;
+  size_t off = 256 + kOrderRegionBytes;
   if (nsplit_eff > 1) {
     w.team = off;
     off = align_up(off + team_region_bytes(pairs, nsplit_eff, gp, d), 256);
@@ -112,11 +134,11 @@ LF_HD inline WorkspaceLayout workspace_layout(int B, int Hkv, int d, int S, int 
   return w;
 }
 
-// Bytes of the workspace a step touches on the team path (header and team
-// region), or with one split (header only).
+// Bytes of the workspace a step touches on the team path (up to the end of
+// the team region), or with one split and no schedule (header only).
 LF_HD inline size_t team_workspace_bytes(int B, int Hkv, int d, int gp, int nsplit_eff) {
   if (nsplit_eff < 2) return 256;
-  return align_up(256 + team_region_bytes((size_t)B * (size_t)Hkv, nsplit_eff, gp, d), 256);
+  return align_up(256 + kOrderRegionBytes + team_region_bytes((size_t)B * (size_t)Hkv, nsplit_eff, gp, d), 256);
 }
 
 // Words of the team region, in this order: published split (max, sum) per
@@ -155,11 +177,12 @@ struct LdsLayout {
 };
 
 constexpr size_t kScratchBytes = 1024;
-// Offsets in the scratch area of the work-item ticket and of the counter
-// that hands phase-K batches to the waves; the decode body's reductions use
-// the bytes below them.
+// Offsets in the scratch area of the work-item ticket, of the counter that
+// hands phase-K batches to the waves and of the pair a ticket stands for;
+// the decode body's reductions use the bytes below them.
 constexpr size_t kTicketSlot = kScratchBytes - 16;
 constexpr size_t kBatchSlot = kScratchBytes - 12;
+constexpr size_t kPairSlot = kScratchBytes - 8;
 // Rows past the end of a split that a wave batch may touch (a batch is 16
 // rows at d = 128, 32 at d = 64, and the last one may run past the split by
 // all but one of its rows); the mask and logit arrays are padded by this

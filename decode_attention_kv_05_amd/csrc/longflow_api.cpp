@@ -236,7 +236,7 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
                  void* v_cache, const uint8_t* mask, uint8_t* mask_w, const void* new_k,
                  const void* new_v, const int32_t* prev_slot, void* out, float* scores,
                  int32_t* evict_slot, void* workspace, int nsplit, int split_path, void* stream,
-                 bool team_only) {
+                 bool team_only, bool schedule) {
   const int G = Hq / Hkv;
   const int gp = lf::padded_group(G);
   int len, eff;
@@ -313,6 +313,14 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
     if (lf::decode_blocks_per_cu(false, d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return LF_E_HIP;
     const int64_t resident = (int64_t)per_cu * cus;
     grid = (int)(resident < nblocks ? resident : nblocks);
+    // With more pairs than workgroups, the workgroups take the pairs in the
+    // order of the previous step's valid extents, longest first, so that
+    // short pairs fill the end of the step (one-split steps of one pair count
+    // sharing the workspace also share the order; it is only a schedule).
+    if (schedule && grid < nblocks && nblocks <= lf::kOrderMaxPairs) {
+      prm.lens = reinterpret_cast<uint32_t*>(ws + wl.order);
+      prm.order = prm.lens + lf::kOrderMaxPairs;
+    }
   }
   return lf::launch_decode(prm, d, gp, nw, nblocks, lds, team_grid, grid, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
@@ -510,9 +518,12 @@ extern "C" int longflow_decode_noalloc(int B, int Hq, int Hkv, int d, int S, flo
   // one of its team waits run out, set exchange words: this call's header
   // and team region start from zero (a fill kernel, so the call can be
   // recorded into a graph; its caller cannot zero a workspace it never sees).
+  // So no pair schedule carries over between calls: a one-split step takes
+  // its pairs in index order and leaves the schedule region alone.
   const size_t clear = team_only ? need : 256;
   if (lf::launch_fill_u32(static_cast<uint32_t*>(ws), clear / 4, 0u, static_cast<hipStream_t>(stream)) != hipSuccess)
     return LF_E_HIP;
   return lf::enqueue_decode_step(B, Hq, Hkv, d, S, scale, q, k_cache, v_cache, mask, nullptr, new_k, new_v,
-                                 prev_slot, out, scores, evict_slot, ws, nsplit, LF_SPLIT_AUTO, stream, team_only);
+                                 prev_slot, out, scores, evict_slot, ws, nsplit, LF_SPLIT_AUTO, stream, team_only,
+                                 false);
 }

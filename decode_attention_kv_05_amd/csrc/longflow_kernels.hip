@@ -721,6 +721,8 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
         if (ff != INT_MAX) next = ff;
       }
       p.evict[pair] = next;
+      // the pair's valid extent, for the next step's longest-first schedule
+      if (p.lens) __hip_atomic_store(p.lens + pair, (uint32_t)n_eff, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else if (SPLIT) {
     // The split's O accumulators, against the split's own max.
@@ -812,6 +814,75 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   }
 }
 
+// Pair indices [first, pairs) into `dst`, sorted by the valid extents in
+// p.lens, longest first (a counting sort over kOrderBins extent classes; the
+// order inside a class is arbitrary).  Each extent is read once, so `dst`
+// is a permutation whatever the words hold: the pairs of this step still
+// running have not written theirs yet, and their previous value (or zero)
+// stands in.
+// Returns false, and writes nothing, when all of them fall in one class (an
+// order would then only cost its lookups).  Uses the first kOrderBins + 1
+// words of LDS; the caller is done with them.
+constexpr int kOrderBins = 512;
+
+template <int NT>
+__device__ __forceinline__ bool build_pair_order(const DecodeParams& p, int first, uint32_t* dst) {
+  static_assert(kOrderMaxPairs % NT == 0 && kOrderBins % 64 == 0, "");
+  constexpr int kPer = kOrderMaxPairs / NT;
+  constexpr int kBinsPerLane = kOrderBins / 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* spread = hist + kOrderBins;  // non-empty classes
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  for (int i = tid; i < kOrderBins; i += NT) hist[i] = 0;
+  int shift = 0;
+  while (((p.S - 1) >> shift) >= kOrderBins) ++shift;
+  __syncthreads();
+  uint32_t bin[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = first + u * NT + tid;
+    if (i < p.pairs) {
+      const uint32_t len = __hip_atomic_load(p.lens + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bin[u] = (uint32_t)(kOrderBins - 1) - min(len >> shift, (uint32_t)(kOrderBins - 1));
+      atomicAdd(hist + bin[u], 1u);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {  // exclusive prefix sum of the class counts
+    uint32_t c[kBinsPerLane], sum = 0, used = 0;
+#pragma unroll
+    for (int r = 0; r < kBinsPerLane; ++r) {
+      c[r] = hist[lane * kBinsPerLane + r];
+      sum += c[r];
+      used += c[r] != 0;
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+      used += __shfl_xor(used, o);
+    }
+    uint32_t at = incl - sum;
+#pragma unroll
+    for (int r = 0; r < kBinsPerLane; ++r) {
+      hist[lane * kBinsPerLane + r] = at;
+      at += c[r];
+    }
+    if (lane == 0) *spread = used;
+  }
+  __syncthreads();
+  if (*spread < 2) return false;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = first + u * NT + tid;
+    if (i < p.pairs) dst[atomicAdd(hist + bin[u], 1u)] = (uint32_t)i;
+  }
+  return true;
+}
+
 // The kernel's parameter block read from the kernarg segment through a
 // pointer the compiler cannot follow (so the loads are not hoisted out of a
 // loop around the call).
@@ -846,23 +917,62 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     // parameter and everything derived from it live across the loop, and
     // the registers the pair needs spill.
     // With at least as many workgroups as pairs the counter is not used.
+    //
+    // Ticket t hands out pair order[t - gridDim.x] when the workspace holds
+    // an order for this launch (pair count and workgroups): the pairs past
+    // the first gridDim.x sorted by their valid extent at the previous step,
+    // longest first, so that short pairs fill the end of the step instead of
+    // a long pair starting last (the ragged batch, 256 sequences of 256..8192
+    // valid slots: 727 us instead of 767).  The first pair stays the block
+    // index, so no workgroup waits for the schedule words to start.  The
+    // workgroup that draws ticket `pairs` (the first to find the queue
+    // empty) builds the next order into the other buffer while the rest
+    // finish their last pairs, and the last workgroup to leave switches
+    // buffers: every claim of this launch has read the switch word by then.
+    // Each buffer has a word of its own naming the launch its order is for
+    // (0: none, or all pairs alike), so the builder can set it at once.
     const bool dynamic = gridDim.x < (unsigned)p.pairs;
+    const uint32_t key = (uint32_t)p.pairs << 16 | gridDim.x;
+    int* tp = tk + (int)((kPairSlot - kTicketSlot) / 4);
     unsigned t = blockIdx.x;
+    int pair = (int)t;
     while (t < (unsigned)p.pairs) {
       const DecodeParams pp = reload_params();
-      decode_pair<D, GP, NW, MODE>(pp, (int)t, (int)t, 0, 1);
+      decode_pair<D, GP, NW, MODE>(pp, pair, pair, 0, 1);
       if (!dynamic) break;
       __syncthreads();  // the pair is done with the LDS
-      if (threadIdx.x == 0) *tk = (int)(gridDim.x + atomicAdd(p.queue, 1u));
+      if (threadIdx.x == 0) {
+        // the schedule words travel with the claim (no wait of their own)
+        uint32_t st = 0, k0 = 0, k1 = 0;
+        if (p.order) {
+          const uint32_t* sw = p.queue + kSchedWord;
+          st = sw[0] & 1u;
+          k0 = sw[1];
+          k1 = sw[2];
+        }
+        const unsigned nt = gridDim.x + atomicAdd(p.queue, 1u);
+        unsigned np = nt;
+        if (nt < (unsigned)p.pairs && (st ? k1 : k0) == key)
+          np = p.order[(size_t)st * kOrderMaxPairs + (nt - gridDim.x)];
+        *tk = (int)nt;
+        *tp = (int)np;
+      }
       __syncthreads();
       t = (unsigned)*tk;
+      pair = *tp;
+    }
+    if (dynamic && p.order && t == (unsigned)p.pairs) {
+      const uint32_t nb = (p.queue[kSchedWord] & 1u) ^ 1u;  // the buffer this launch does not read
+      const bool built = build_pair_order<NW * 64>(p, (int)gridDim.x, p.order + (size_t)nb * kOrderMaxPairs);
+      if (threadIdx.x == 0) atomicExch(p.queue + kSchedWord + 1 + nb, built ? key : 0u);
     }
     // Every workgroup has made its last claim once all have counted
     // themselves out, so the last one can leave the counters at zero for the
-    // next launch.
+    // next launch (and flip the schedule's switch word without reading it).
     if (dynamic && threadIdx.x == 0 && atomicAdd(p.queue + 1, 1u) == gridDim.x - 1) {
       atomicExch(p.queue, 0u);
       atomicExch(p.queue + 1, 0u);
+      if (p.order) atomicXor(p.queue + kSchedWord, 1u);
     }
   } else if constexpr (MODE == kModeTeam) {
     // Work items go out by tickets in the order workgroups start, not by

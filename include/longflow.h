@@ -58,9 +58,15 @@
  * Workspace: zero-filled before its first use (lf_workspace_init, or any
  * zeroing of the memory).  It holds the device status word, the work-item
  * counters of the one-split step and the team path's exchange words, which
- * every completed call leaves at zero for the next; everything else in it is
- * scratch for the duration of a call.  After a step that reports
- * LF_DEV_TEAM_TIMEOUT, zero it again before its next use.
+ * every completed call leaves at zero for the next, and the one-split step's
+ * pair schedule: each such step with more (sequence, KV head) pairs than
+ * the device holds workgroups at once (and at most 4096 of them) records
+ * every pair's valid extent there, and the next one of the same pair count
+ * hands out its pairs longest first.  The schedule only orders work:
+ * results do not depend on it, and any calls that keep their workspace may
+ * share it.  Everything else in the workspace is scratch for the duration
+ * of a call.  After a step that reports LF_DEV_TEAM_TIMEOUT, zero it again
+ * before its next use.
  *
  * Errors: every entry point returns LF_OK (0) or a negative lf_status code
  * from host-side checks made before anything is enqueued; nothing is enqueued
@@ -275,12 +281,13 @@ int lf_read_device_status(const void* workspace, void* stream, uint32_t* flags);
  * arguments, shapes, plan and results as longflow_decode (the same kernels);
  * the workspace is the library's own LF_STATIC_SCRATCH_BYTES device array,
  * whose header (and, on the team path, exchange region) a fill kernel on
- * `stream` clears at the start of every call.  The
+ * `stream` clears at the start of every call; so it keeps no pair schedule
+ * between calls (a one-split step takes its pairs in index order).  The
  * call allocates nothing and makes no allocating library call; the array's
  * device address is looked up on the first call on each device.
  * A step that needs more scratch than the array holds returns LF_E_SCRATCH
  * before anything is enqueued: a one-split step needs 256 bytes; a split step
- * on the team path 256 bytes plus its exchange region (about 8.3 KB per
+ * on the team path 48.25 KB plus its exchange region (about 8.3 KB per
  * (sequence, KV head) and split at 8 query heads per KV head and d = 128:
  * 4.3 MB for 16 x 8 pairs in 4 splits); a split step that cannot take the
  * team path, its whole combine workspace (lf_workspace_size).

@@ -219,19 +219,25 @@ def test_general_entry_argument_errors():
     assert _ex_call(f, shape=(0, 8, 2, 128, 100), split_path=2, **zeros) == lf.LF_OK
 
 
+# The one-split pair schedule after the 256-byte header: for up to 4096
+# pairs, a 32-bit valid extent each and two 32-bit pair-order buffers.
+ORDER_REGION = 3 * 4096 * 4
+
+
 def test_fill_workspace_has_free_slot_minima():
-    """Split workspaces hold one 32-bit lowest-free-slot word per combine chunk,
+    """Every workspace holds the 256-byte header and the one-split pair
+    schedule; split workspaces then hold one 32-bit lowest-free-slot word per combine chunk,
     then the team path's exchange region: per split of a pair 64-bit words for
     its (max, sum) per padded head, its three results and its O accumulators,
     one 32-bit counter per pair and eight 32-bit ticket counters."""
     B, Hq, Hkv, d, S = 4, 16, 2, 128, 5000
     one = lf.lf_workspace_size(B, Hq, Hkv, d, S, 1)
-    assert one == 256
+    assert one == 256 + ORDER_REGION
     chunks = -(-S // 2048)
     pairs = B * Hkv
     gp = 8
     split = 3
-    expect = 256
+    expect = 256 + ORDER_REGION
     for n in (pairs * split * gp * 2 * 4, pairs * split * gp * d * 4, pairs * S * gp * 4, pairs * S * 4,
               pairs * chunks * 8, pairs * chunks * 4, pairs * split * (gp * 2 + 3 + gp * d) * 8 + pairs * 4 + 8 * 4):
         expect += -(-n // 256) * 256
@@ -336,8 +342,9 @@ _LAYOUT_CHECK = r"""
 #include <cstdlib>
 #include "layout.h"
 // Every workspace region of a split step lies inside the workspace, is
-// aligned for its element type and overlaps no other region; the team
-// region holds exactly its words and the fill of zero_words covers it.
+// aligned for its element type and overlaps no other region (the one-split
+// schedule region included); the team region holds exactly its words and
+// the fill of zero_words covers it.
 int main() {
   int bad = 0, cases = 0;
   const int Bs[] = {1, 2, 3, 16, 128, 257}, Hkvs[] = {1, 2, 8}, gs[] = {1, 2, 3, 4, 8}, ds[] = {64, 128};
@@ -355,9 +362,14 @@ int main() {
       {w.part_ml, pairs * eff * gp * 2 * 4, 4}, {w.part_o, pairs * eff * gp * (size_t)d * 4, 4},
       {w.logit, pairs * (size_t)S * gp * 4, 16}, {w.vnorm, pairs * (size_t)S * 4, 4},
       {w.cand, pairs * (size_t)lf::combine_chunks(S) * 8, 8}, {w.ffree, pairs * (size_t)lf::combine_chunks(S) * 4, 4},
-      {w.team, lf::team_region_bytes(pairs, eff, gp, d), 8}};
+      {w.team, lf::team_region_bytes(pairs, eff, gp, d), 8}, {w.order, lf::kOrderRegionBytes, 4}};
     const int nr = sizeof(r) / sizeof(r[0]);
     ++cases;
+    // the schedule region sits at the same place in one-split layouts, and
+    // a team step's share of the workspace reaches past its team words
+    const lf::WorkspaceLayout w1 = lf::workspace_layout(B, Hkv, d, S, gp, 1);
+    if (w1.order != 256 || w1.total != 256 + lf::kOrderRegionBytes || w.order != w1.order) ++bad;
+    if (lf::team_workspace_bytes(B, Hkv, d, gp, eff) < w.team + lf::team_region_bytes(pairs, eff, gp, d)) ++bad;
     for (int i = 0; i < nr; ++i) {
       if (r[i].off < 256 || r[i].off + r[i].bytes > w.total || r[i].off % r[i].align) ++bad;
       for (int k = i + 1; k < nr; ++k)
@@ -381,8 +393,8 @@ int main() {
 
 
 def test_workspace_regions_fit_and_do_not_overlap(tmp_path):
-    """Host C++ check of the workspace layout of split steps (combine and
-    team regions) over a grid of shapes and split counts."""
+    """Host C++ check of the workspace layout of split steps (schedule,
+    combine and team regions) over a grid of shapes and split counts."""
     import shutil
     import subprocess
     gxx = shutil.which("g++")
@@ -426,7 +438,7 @@ def test_workspace_size_for_the_device_plan_needs_a_device():
     out = ctypes.c_size_t(0)
     rc = lf._lib.lf_workspace_size(128, 32, 8, 128, 3200, 0, ctypes.byref(out))
     assert rc == lf.LF_E_HIP
-    assert lf.lf_workspace_size(128, 32, 8, 128, 3200, 1) == 256
+    assert lf.lf_workspace_size(128, 32, 8, 128, 3200, 1) == 256 + ORDER_REGION
 
 
 def test_library_records_its_source_hash():

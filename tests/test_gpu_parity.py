@@ -326,9 +326,10 @@ def test_team_path_replays_in_a_graph():
     (2, 32, 8, 8192, 4, "team"), (3, 16, 4, 1500, 5, "team"), (16, 64, 8, 4096, 64, "team"),
     (2, 32, 8, 8192, 4, "combine"), (512, 32, 8, 256, 1, None), (1, 4, 1, 256, 1, None)])
 def test_workspace_left_zero(B, Hq, Hkv, S, nsplit, path):
-    """Every completed step leaves the whole workspace at zero: the status
-    word (no flags), the persistent workgroups' counters (the 4096-pair case
-    has more pairs than workgroups, so they are used), the team path's
+    """Every completed step leaves the workspace at zero but for the one-split
+    pair schedule: the status word (no flags), the persistent workgroups'
+    counters (the 4096-pair case has more pairs than workgroups, so they are
+    used), the team path's
     exchange words, arrival and ticket counters (the 64-split case has more
     teams than the device holds at once) and, on team steps, the combine
     path's untouched arrays; on combine steps, the header.  So the next step
@@ -347,7 +348,105 @@ def test_workspace_left_zero(B, Hq, Hkv, S, nsplit, path):
         prev = ev
         torch.cuda.synchronize()
         # the combine path's arrays (past the header and the team region) are
-        # its scratch; check its header only
-        kept = ws[:256] if path == "combine" else ws
+        # its scratch; check its header only.  One-split steps keep their
+        # pair schedule: three header words at byte 128 and the
+        # schedule region after the header.
+        kept = ws[:256] if path == "combine" else ws.clone()
+        if path is None:
+            kept[128:140] = 0
+            kept[256:256 + 3 * 4096 * 4] = 0
         nz = torch.nonzero(kept).flatten()
         assert nz.numel() == 0, f"step {t}: {nz.numel()} nonzero workspace bytes, first at {nz[:8].tolist()}"
+
+
+def test_longest_first_schedule():
+    """Steps that share a workspace hand out their pairs longest first from
+    the second step on.  After each step the workspace holds every pair's
+    valid extent, a switch word naming the order buffer the next step reads
+    and that buffer's launch key (pairs << 16 | workgroups); after the second
+    step the buffer is a permutation of the pairs past the first workgroups'
+    (which take their block index) in non-increasing extent (to within a
+    class of S / 512 slots).  The results equal, bit for bit, those of steps
+    that each start from a fresh workspace (pairs in index order), also when
+    a step of another pair count (which builds its own order) comes between.
+    A batch whose pairs all have one extent keeps no order.
+    1024 pairs of up to 2048 slots: more pairs than the device holds
+    workgroups of this size at once, so the work-item counter is used."""
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("schedule", B=128, Hq=64, Hkv=8, d=128, S=2048, steps=4, kind="ragged", seed=9900, len_lo=8)
+    other = wl.replace(name="schedule_b96", B=96, seed=9901)
+    k, v, mask = W.initial_cache(wl)
+    ko, vo, masko = W.initial_cache(other)
+    pairs = wl.B * wl.Hkv
+    dm = torch.from_numpy(mask).cuda()
+    ka, va, kb, vb = bf16_dev(k), bf16_dev(v), bf16_dev(k), bf16_dev(v)
+    ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, 1)
+    extent = np.array([np.flatnonzero(mask[b]).max() + 1 for b in range(wl.B)], dtype=np.int64)
+    extent = np.repeat(extent, wl.Hkv)
+    prev_a = prev_b = torch.from_numpy(W.first_prev_slot(wl)).cuda()
+    words = lambda: ws[128:140].view(torch.int32).cpu().numpy()
+    st = 0  # expected switch word: each step builds into the buffer it does not read, then flips it
+    for t in range(wl.steps):
+        log(f"schedule step {t}")
+        q, nk, nv = (bf16_dev(x) for x in W.step_inputs(wl, t))
+        oa, sa, ea = lf.longflow_decode(q, ka, va, dm, nk, nv, prev_a, scale=float(wl.scale), workspace=ws, nsplit=1)
+        ob, sb, eb = lf.longflow_decode(q, kb, vb, dm, nk, nv, prev_b, scale=float(wl.scale), nsplit=1)
+        torch.cuda.synchronize()
+        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), f"step {t}: O differs"
+        assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), f"step {t}: scores differ"
+        assert torch.equal(ea, eb), f"step {t}: evicted slots differ"
+        prev_a, prev_b = ea, eb
+        w = words()
+        c = ws[16:28].view(torch.int32).cpu().numpy()
+        assert not c.any(), f"step {t}: counters {c} not reset"
+        st ^= 1
+        key = int(w[1 + st])
+        grid = key & 0xFFFF
+        assert w[0] == st and key >> 16 == pairs and 0 < grid < pairs, f"step {t}: schedule words {w}"
+        lens = ws[256:256 + 4 * pairs].view(torch.int32).cpu().numpy()
+        assert np.array_equal(lens, extent), f"step {t}: valid extents"
+        if t in (1, 3):  # built from the extents of a previous step of this batch
+            buf = int(w[0])
+            at = 256 + (1 + buf) * 4096 * 4
+            order = ws[at:at + 4 * (pairs - grid)].view(torch.int32).cpu().numpy()
+            assert np.array_equal(np.sort(order), np.arange(grid, pairs)), f"step {t}: order is not a permutation"
+            # longest first to within the sort's class width: 512 classes
+            # over the S slots (4 slots wide here)
+            shift = next(x for x in range(32) if (wl.S - 1) >> x < 512)
+            assert np.all(np.diff(extent[order] >> shift) <= 0), f"step {t}: order not longest first"
+        if t == 1:
+            # a step of another pair count on the same workspace: its own
+            # order, then the first count starts over from index order
+            log("schedule: 768-pair step in between")
+            qo, nko, nvo = (bf16_dev(x) for x in W.step_inputs(other, 0))
+            po = torch.from_numpy(W.first_prev_slot(other)).cuda()
+            dko, dvo, dmo = bf16_dev(ko), bf16_dev(vo), torch.from_numpy(masko).cuda()
+            r1 = lf.longflow_decode(qo, dko, dvo, dmo, nko, nvo, po, scale=float(other.scale), workspace=ws, nsplit=1)
+            r2 = lf.longflow_decode(qo, bf16_dev(ko), bf16_dev(vo), dmo, nko, nvo, po, scale=float(other.scale),
+                                    nsplit=1)
+            torch.cuda.synchronize()
+            assert torch.equal(r1[0].view(torch.int16), r2[0].view(torch.int16))
+            assert torch.equal(r1[1].view(torch.int32), r2[1].view(torch.int32)) and torch.equal(r1[2], r2[2])
+            w = words()
+            st ^= 1
+            assert w[0] == st and w[1 + st] >> 16 == 96 * 8, f"768-pair step: schedule words {w}"
+            del dko, dvo
+    assert torch.equal(ka.view(torch.int16), kb.view(torch.int16)) and torch.equal(va.view(torch.int16),
+                                                                                  vb.view(torch.int16))
+    assert lf.lf_read_device_status(ws) == 0
+    del ka, va, kb, vb, k, v, ko, vo
+    # all pairs of one extent: no order is kept (its lookups would only cost)
+    plain = wl.replace(name="schedule_plain", kind="plain", seed=9902)
+    kp, vp, mp = W.initial_cache(plain)
+    dkp, dvp, dmp = bf16_dev(kp), bf16_dev(vp), torch.from_numpy(mp).cuda()
+    wsp = lf.new_workspace(plain.B, plain.Hq, plain.Hkv, plain.d, plain.S, 1)
+    prev = torch.from_numpy(W.first_prev_slot(plain)).cuda()
+    for t in range(3):
+        log(f"schedule plain step {t}")
+        q, nk, nv = (bf16_dev(x) for x in W.step_inputs(plain, t))
+        _, _, prev = lf.longflow_decode(q, dkp, dvp, dmp, nk, nv, prev, scale=float(plain.scale), workspace=wsp,
+                                        nsplit=1)
+        w = wsp[128:140].view(torch.int32).cpu().numpy()
+        # (the first step's builder may still read extents of zero for pairs
+        # that have not started)
+        assert w[0] == (t + 1) % 2 and (t == 0 or w[1 + w[0]] == 0), f"plain step {t}: schedule words {w}"
