@@ -385,31 +385,42 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   // The split that owns prev_slot overwrites that cache row before anything
   // reads it: the barrier after the mask staging makes the workgroup's global
   // writes visible to all of its threads, so the row is then streamed like any
-  // other (no other workgroup reads it during this step).
+  // other (no other workgroup reads it during this step).  The new row, the
+  // slot and the first block of the split's mask are all requested before
+  // the row is written: the mask loads could not move above those stores
+  // (a byte load may alias them), and one round trip to memory then covers
+  // what took three.
   const int prev = p.prev[pair];
+  const uint8_t* src = mrow + s0;
+  uint8_t m0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = u * kThreads + tid;
+    m0[u] = i < n ? src[i] : 0;
+  }
+  uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
+  if (tid < D / 8) {
+    kx = reinterpret_cast<const uint4*>(nk)[tid];
+    vx = reinterpret_cast<const uint4*>(nv)[tid];
+  }
+  const bool owns_prev = prev >= s0 && prev < s0 + n;
   if (prev != -1) {
     if (prev < 0 || prev >= p.S) {
       if (sp == 0 && tid == 0) atomicOr(p.status, LF_DEV_BAD_PREV);
-    } else if (prev >= s0 && prev < s0 + n) {
+    } else if (owns_prev) {
       if (tid < D / 8) {
-        const uint4 kx = reinterpret_cast<const uint4*>(nk)[tid];
-        const uint4 vx = reinterpret_cast<const uint4*>(nv)[tid];
         reinterpret_cast<uint4*>(p.k + (row0 + prev) * D)[tid] = kx;
         reinterpret_cast<uint4*>(p.v + (row0 + prev) * D)[tid] = vx;
       }
-      if (tid == 0 && mrow[prev] == 0) {
-        if (p.fill) {
-          // A free slot: it joins the mask.  The mask is shared by the KV
-          // heads, so all of them must be writing this same slot.
-          p.mask_w[(size_t)b * p.S + prev] = 1;
-          for (int jj = 0; jj < p.Hkv; ++jj)
-            if (p.prev[(size_t)b * p.Hkv + jj] != prev) {
-              atomicOr(p.status, LF_DEV_FILL_DIVERGED);
-              break;
-            }
-        } else {
-          atomicOr(p.status, LF_DEV_WRITE_MASKED);
-        }
+      if (p.fill && tid == 0 && mrow[prev] == 0) {
+        // A free slot: it joins the mask.  The mask is shared by the KV
+        // heads, so all of them must be writing this same slot.
+        p.mask_w[(size_t)b * p.S + prev] = 1;
+        for (int jj = 0; jj < p.Hkv; ++jj)
+          if (p.prev[(size_t)b * p.Hkv + jj] != prev) {
+            atomicOr(p.status, LF_DEV_FILL_DIVERGED);
+            break;
+          }
       }
     }
   }
@@ -421,16 +432,16 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   if (tid == 0) *kq = 0;
   int last_valid = -1;
   int first_free = INT_MAX;
-  const int own = (p.fill && prev >= s0 && prev < s0 + n) ? prev - s0 : -1;
+  const int own = (p.fill && owns_prev) ? prev - s0 : -1;
   {
-    const uint8_t* src = mrow + s0;
     const int npad = n + kRowPad;
     for (int base = 0; base < npad; base += kThreads * 8) {
       uint8_t t8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = base + u * kThreads + tid;
-        t8[u] = i < n ? (uint8_t)(src[i] | (i == own)) : 0;
+        const uint8_t raw = base == 0 ? m0[u] : (i < n ? src[i] : 0);
+        t8[u] = i < n ? (uint8_t)(raw | (i == own)) : 0;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -450,6 +461,9 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     }
   }
   __syncthreads();
+  // A write into a masked slot (outside the fill step) is flagged from the
+  // staged mask.
+  if (!p.fill && owns_prev && tid == 0 && mk[prev - s0] == 0) atomicOr(p.status, LF_DEV_WRITE_MASKED);
   int n_eff = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) n_eff = max(n_eff, red_i[w] + 1);
@@ -536,8 +550,26 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     // Rows up to the end of the last batch (all written in phase K, -inf
     // when invalid) become e = exp2(s - split max); invalid ones become
     // exactly 0, so phase V needs no per-row select.
+    // Four rows per thread at a time, their LDS reads issued together (one
+    // row at a time, each read waited for the previous row's write); the
+    // sum still adds the rows in the same order.
     const int covered = (n_eff + ROWS - 1) / ROWS * ROWS;
-    for (int r = tid / GP; r < covered; r += kThreads / GP) {
+    constexpr int kStride = kThreads / GP;
+    int r = tid / GP;
+    for (; r + 3 * kStride < covered; r += 4 * kStride) {
+      float sv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sv[q] = lg[(r + q * kStride) * GP + h];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rq = r + q * kStride;
+        const float e = (sv[q] == kNegInf) ? 0.f : exp2f(sv[q] - mh);
+        lg[rq * GP + h] = e;
+        lsum += e;
+        if (SPLIT && rq < n_eff) wl[rq * GP + h] = e;
+      }
+    }
+    for (; r < covered; r += kStride) {
       const float s = lg[r * GP + h];
       const float e = (s == kNegInf) ? 0.f : exp2f(s - mh);
       lg[r * GP + h] = e;
@@ -675,7 +707,15 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     // Rows at or past n_eff are all masked: score +inf, no |v|_1 needed.
     float* dst = SPLIT ? p.ws_vnorm + row0 + s0 : p.scores + row0 + s0;
     const int lim = SPLIT ? n_eff : n;
-    for (int r = tid; r < lim; r += kThreads) dst[r] = r < n_eff ? lg[r * GP] : kInf;
+    int r = tid;
+    for (; r + 3 * kThreads < lim; r += 4 * kThreads) {
+      float sv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sv[q] = lg[(r + q * kThreads) * GP];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[r + q * kThreads] = r + q * kThreads < n_eff ? sv[q] : kInf;
+    }
+    for (; r < lim; r += kThreads) dst[r] = r < n_eff ? lg[r * GP] : kInf;
   }
 
   // ---- O: fold the row groups of each wave, then the waves through LDS
