@@ -319,6 +319,27 @@ __device__ __forceinline__ float team_wait(const uint64_t* w, uint32_t* status, 
   return __builtin_nanf("");
 }
 
+// Up to 8 published words from each of K arrays, w[k][i * stride[k]] for
+// i < n, with all their loads in flight at once (one round trip to memory
+// where word-by-word waits took one each); words not yet ready are then
+// waited for one by one.  out[k][i] for i >= n is unspecified.
+template <int K>
+__device__ __forceinline__ void team_read8(const uint64_t* const (&w)[K], const size_t (&stride)[K], int n,
+                                           float (&out)[K][8], uint32_t* status, uint64_t deadline) {
+  uint64_t v[K][8];
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[k][i] = i < n ? __hip_atomic_load(w[k] + i * stride[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kReady;
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      out[k][i] = (v[k][i] & kReady) ? __uint_as_float((uint32_t)v[k][i])
+                                     : team_wait(w[k] + i * stride[k], status, deadline);
+}
+
 // One (pair, split) of a decode step.
 template <int D, int GP, int NW, int MODE>
 __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int pair, int sp, int nsplit) {
@@ -669,15 +690,41 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     // when its logits are NaN).  c turns this split's e into probabilities:
     // p = e * exp2(split max - pair max) / L.
     if (tid < GP) {
-      const uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2;
+      // this head's (max, sum) words: split q's at xs + q * GP * 2
+      const uint64_t* xs = p.xstat + (size_t)pair * nsplit * GP * 2 + tid * 2;
+      const size_t st2[2] = {(size_t)GP * 2, (size_t)GP * 2};
       const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kTeamWaitTicks;
       float gm = kNegInf;
-      for (int q = 0; q < nsplit; ++q) gm = fmaxf(gm, team_wait(xs + (q * GP + tid) * 2, p.status, deadline));
       float gl = 0.f;
-      for (int q = 0; q < nsplit; ++q) {
-        const float mq = team_wait(xs + (q * GP + tid) * 2, p.status, deadline);
-        const float lq = team_wait(xs + (q * GP + tid) * 2 + 1, p.status, deadline);
-        gl = mq != kNegInf ? fmaf(lq, exp2f(mq - gm), gl) : gl + lq;
+      if (nsplit <= 8) {  // every word in one batch
+        float ml[2][8];
+        const uint64_t* w2[2] = {xs, xs + 1};
+        team_read8<2>(w2, st2, nsplit, ml, p.status, deadline);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nsplit) gm = fmaxf(gm, ml[0][i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nsplit) gl = ml[0][i] != kNegInf ? fmaf(ml[1][i], exp2f(ml[0][i] - gm), gl) : gl + ml[1][i];
+      } else {  // the maxima 8 splits at a time, then the sums
+        for (int q0 = 0; q0 < nsplit; q0 += 8) {
+          float m[1][8];
+          const uint64_t* w1[1] = {xs + (size_t)q0 * GP * 2};
+          const size_t st1[1] = {(size_t)GP * 2};
+          team_read8<1>(w1, st1, nsplit - q0, m, p.status, deadline);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (q0 + i < nsplit) gm = fmaxf(gm, m[0][i]);
+        }
+        for (int q0 = 0; q0 < nsplit; q0 += 8) {
+          float ml[2][8];
+          const uint64_t* w2[2] = {xs + (size_t)q0 * GP * 2, xs + (size_t)q0 * GP * 2 + 1};
+          team_read8<2>(w2, st2, nsplit - q0, ml, p.status, deadline);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (q0 + i < nsplit)
+              gl = ml[0][i] != kNegInf ? fmaf(ml[1][i], exp2f(ml[0][i] - gm), gl) : gl + ml[1][i];
+        }
       }
       const float gil = (gl > 0.f || gl != gl) ? 1.0f / gl : 0.f;
       const float ms = stat_m[tid];
@@ -813,10 +860,14 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
         const float gm = stat_m[h];
         float o = 0.f;
         if (gm != kNegInf) {
-          for (int q = 0; q < nsplit; ++q) {
-            const float mq = team_wait(xs + (q * GP + h) * 2, p.status, deadline);
-            const float pv = team_wait(xa + (size_t)q * GP * D + idx, p.status, deadline);
-            if (mq != kNegInf) o = fmaf(pv, exp2f(mq - gm), o);
+          for (int q0 = 0; q0 < nsplit; q0 += 8) {  // 8 splits' words per batch
+            float mp[2][8];
+            const uint64_t* w2[2] = {xs + ((size_t)q0 * GP + h) * 2, xa + (size_t)q0 * GP * D + idx};
+            const size_t st2[2] = {(size_t)GP * 2, (size_t)GP * D};
+            team_read8<2>(w2, st2, nsplit - q0, mp, p.status, deadline);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (q0 + i < nsplit && mp[0][i] != kNegInf) o = fmaf(mp[1][i], exp2f(mp[0][i] - gm), o);
           }
         }
         p.out[((size_t)b * p.Hq + (size_t)j * p.G + h) * D + (idx - h * D)] = f32_to_bf16_rne(o * stat_il[h]);
@@ -824,13 +875,19 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
       if (tid == 0) {
         uint64_t m = kNoCandidate;
         uint32_t ff = (uint32_t)INT_MAX;
-        for (int q = 0; q < nsplit; ++q) {
-          const uint64_t* xf = p.xfin + ((size_t)pair * nsplit + q) * 3;
-          const uint64_t hi = __float_as_uint(team_wait(xf, p.status, deadline));
-          const uint64_t lo = __float_as_uint(team_wait(xf + 1, p.status, deadline));
-          const uint64_t cq = hi << 32 | lo;
-          m = cq < m ? cq : m;
-          ff = min(ff, __float_as_uint(team_wait(xf + 2, p.status, deadline)));
+        for (int q0 = 0; q0 < nsplit; q0 += 8) {
+          const uint64_t* xf = p.xfin + ((size_t)pair * nsplit + q0) * 3;
+          float r[3][8];
+          const uint64_t* w3[3] = {xf, xf + 1, xf + 2};
+          const size_t st3[3] = {3, 3, 3};
+          team_read8<3>(w3, st3, nsplit - q0, r, p.status, deadline);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (q0 + i >= nsplit) break;
+            const uint64_t cq = (uint64_t)__float_as_uint(r[0][i]) << 32 | __float_as_uint(r[1][i]);
+            m = cq < m ? cq : m;
+            ff = min(ff, __float_as_uint(r[2][i]));
+          }
         }
         int32_t next = m == kNoCandidate ? -1 : (int32_t)(uint32_t)m;
         if (p.fill && ff != (uint32_t)INT_MAX) next = (int32_t)ff;
