@@ -324,12 +324,14 @@ def test_team_path_replays_in_a_graph():
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,nsplit,path", [
     (2, 32, 8, 8192, 4, "team"), (3, 16, 4, 1500, 5, "team"), (16, 64, 8, 4096, 64, "team"),
-    (2, 32, 8, 8192, 4, "combine"), (512, 32, 8, 256, 1, None), (1, 4, 1, 256, 1, None)])
+    (2, 32, 8, 8192, 4, "combine"), (512, 32, 8, 256, 1, None), (600, 32, 8, 128, 1, None),
+    (1, 4, 1, 256, 1, None)])
 def test_workspace_left_zero(B, Hq, Hkv, S, nsplit, path):
     """Every completed step leaves the workspace at zero but for the one-split
     pair schedule: the status word (no flags), the persistent workgroups'
     counters (the 4096-pair case has more pairs than workgroups, so they are
-    used), the team path's
+    used; the 4800-pair case has more pairs than the schedule takes, so its
+    workspace stays all zero), the team path's
     exchange words, arrival and ticket counters (the 64-split case has more
     teams than the device holds at once) and, on team steps, the combine
     path's untouched arrays; on combine steps, the header.  So the next step
@@ -352,7 +354,7 @@ def test_workspace_left_zero(B, Hq, Hkv, S, nsplit, path):
         # pair schedule: three header words at byte 128 and the
         # schedule region after the header.
         kept = ws[:256] if path == "combine" else ws.clone()
-        if path is None:
+        if path is None and B * Hkv <= 4096:  # (more pairs than that keep no schedule)
             kept[128:140] = 0
             kept[256:256 + 3 * 4096 * 4] = 0
         nz = torch.nonzero(kept).flatten()
@@ -450,3 +452,36 @@ def test_longest_first_schedule():
         # (the first step's builder may still read extents of zero for pairs
         # that have not started)
         assert w[0] == (t + 1) % 2 and (t == 0 or w[1 + w[0]] == 0), f"plain step {t}: schedule words {w}"
+
+
+def test_longest_first_schedule_fill_step():
+    """Fill steps that share a workspace (pairs handed out longest first from
+    the second step on) give the same outputs, cache and mask updates, bit for
+    bit, as fill steps that each start from a fresh workspace.  1024 pairs of
+    a ragged batch with free slots, four steps."""
+    from decode_attention_kv_05_amd import longflow as lf
+    wl = W.Workload("schedule_fill", B=128, Hq=64, Hkv=8, d=128, S=2048, steps=4, kind="ragged", seed=9910,
+                    len_lo=8)
+    k, v, mask = W.initial_cache(wl)
+    ka, va, kb, vb = bf16_dev(k), bf16_dev(v), bf16_dev(k), bf16_dev(v)
+    ma, mb = torch.from_numpy(mask.copy()).cuda(), torch.from_numpy(mask.copy()).cuda()
+    ws = lf.new_workspace(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, 1)
+    free = [np.flatnonzero(mask[b] == 0) for b in range(wl.B)]
+    first_free = np.array([f[0] if f.size else -1 for f in free], dtype=np.int32)
+    prev_a = prev_b = torch.from_numpy(np.repeat(first_free[:, None], wl.Hkv, axis=1)).cuda()
+    for t in range(wl.steps):
+        log(f"schedule fill step {t}")
+        q, nk, nv = (bf16_dev(x) for x in W.step_inputs(wl, t))
+        oa, sa, na = lf.longflow_decode_fill(q, ka, va, ma, nk, nv, prev_a, scale=float(wl.scale), workspace=ws,
+                                             nsplit=1)
+        ob, sb, nb = lf.longflow_decode_fill(q, kb, vb, mb, nk, nv, prev_b, scale=float(wl.scale), nsplit=1)
+        torch.cuda.synchronize()
+        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), f"step {t}: O differs"
+        assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), f"step {t}: scores differ"
+        assert torch.equal(na, nb) and torch.equal(ma, mb), f"step {t}: next slots or masks differ"
+        prev_a, prev_b = na, nb
+    w = ws[128:140].view(torch.int32).cpu().numpy()
+    assert w[1 + w[0]] >> 16 == wl.B * wl.Hkv, f"no order kept: schedule words {w}"
+    assert torch.equal(ka.view(torch.int16), kb.view(torch.int16)) and torch.equal(va.view(torch.int16),
+                                                                                  vb.view(torch.int16))
+    assert lf.lf_read_device_status(ws) == 0
