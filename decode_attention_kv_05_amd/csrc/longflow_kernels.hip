@@ -539,8 +539,29 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
   // Phase V keeps a fixed share of rows per wave (rows wave * ROWS + k *
   // stride), so each lane's O accumulators sum the same rows in the same
   // order every time and O is the same bit for bit from run to run.
-  const int nbatch = wave * ROWS < n_eff ? (n_eff - wave * ROWS + stride - 1) / stride : 0;
-  const int rot = MODE != kModeSingle && nbatch > 0 ? (int)(((unsigned)item * kRotate) % (unsigned)nbatch) : 0;
+  //
+  // A SIMD serves its waves oldest first, and waves w, w + 4, w + 8, w + 12
+  // share one, so with equal shares the later waves end phase V last (on
+  // the 16-wave team kernel waves 12-15 ended about 8.5 us after waves 0-3).
+  // The team kernel therefore gives the last eighth of the batches to the
+  // older half of the waves only: batch b < nbv - tailn goes to wave
+  // b % NW, batch nbv - tailn + t to wave t % (NW / 2).  The shares stay a
+  // fixed function of the wave and the row count.
+  constexpr bool kSkew = MODE == kModeTeam && NW == 16;
+  int nbatch, nmain = 0, mainn = 0, wv = 0;
+  if constexpr (kSkew) {
+    wv = __builtin_amdgcn_readfirstlane(wave);
+    const int nbv = (n_eff + ROWS - 1) / ROWS;
+    const int tailn = nbv / 8;
+    mainn = nbv - tailn;
+    nmain = wv < mainn ? (mainn - wv + NW - 1) / NW : 0;
+    const int ntail = wv < NW / 2 && wv < tailn ? (tailn - wv + NW / 2 - 1) / (NW / 2) : 0;
+    nbatch = nmain + ntail;
+  } else {
+    nbatch = wave * ROWS < n_eff ? (n_eff - wave * ROWS + stride - 1) / stride : 0;
+    nmain = nbatch;
+  }
+  const int rot = MODE != kModeSingle && nmain > 0 ? (int)(((unsigned)item * kRotate) % (unsigned)nmain) : 0;
 
   // ---- softmax statistics of this split
   // Lanes with equal c hold the same heads; fold the row groups, then waves.
@@ -657,7 +678,13 @@ __device__ __forceinline__ void decode_pair(const DecodeParams& p, int item, int
     }
   };
   for (int bi = 0; bi < nbatch; ++bi) {
-    const int r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
+    int r0;
+    if constexpr (kSkew) {
+      r0 = (bi < nmain ? wv + (bi + rot < nmain ? bi + rot : bi + rot - nmain) * NW
+                       : mainn + wv + (bi - nmain) * (NW / 2)) * ROWS;
+    } else {
+      r0 = wave * ROWS + (bi + rot < nbatch ? bi + rot : bi + rot - nbatch) * stride;
+    }
     uint4 vbuf[U];
     const uint32_t vok = load_batch<D, U, RPW>(vbuf, vrs, mk, r0, rg, c);
     float* lrow = lg + (r0 + rg) * GP;
