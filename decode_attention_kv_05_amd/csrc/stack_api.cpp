@@ -20,7 +20,7 @@ namespace {
 constexpr int kMaxStackBatch = 256;  // two 128-row blocks of the projection kernel
 
 struct StackLayout {
-  size_t dec, q, k, v, o, x0, x1, scores, part, total;
+  size_t dec, q, k, v, o, x0, x1, scores, rope, part, total;
 };
 
 StackLayout stack_layout(int B, int H, int Hq, int Hkv, int d, int S, size_t dec_bytes) {
@@ -39,6 +39,7 @@ StackLayout stack_layout(int B, int H, int Hq, int Hkv, int d, int S, size_t dec
   w.x0 = take((size_t)B * H * 2);
   w.x1 = take((size_t)B * H * 2);
   w.scores = take((size_t)B * Hkv * S * 4);
+  w.rope = take((size_t)B * (d / 2) * 8);
   const size_t p1 = lf::gemm_partial_bytes(B, (Hq + 2 * Hkv) * d, H);
   const size_t p2 = lf::gemm_partial_bytes(B, H, Hq * d);
   w.part = take(p1 > p2 ? p1 : p2);
@@ -159,14 +160,16 @@ int enqueue_stack(const StackArgs& a, hipStream_t s) {
   uint16_t* xb[2] = {reinterpret_cast<uint16_t*>(ws + wl.x0), reinterpret_cast<uint16_t*>(ws + wl.x1)};
   float* ws_scores = reinterpret_cast<float*>(ws + wl.scores);
   float* part = reinterpret_cast<float*>(ws + wl.part);
+  float2* rope = reinterpret_cast<float2*>(ws + wl.rope);
   const int nq = (a.Hq + 2 * a.Hkv) * a.d;
-  const double log2_base = std::log2((double)a.rope_base);
+  const lf::RopeParams rp{a.pos, rope, q, kn, vn, a.B, a.Hq, a.Hkv, a.d, std::log2((double)a.rope_base)};
 
+  // The positions hold for every layer of the step: one rotation table.
+  if (lf::launch_rope_table(rp, s) != hipSuccess) return LF_E_HIP;
   for (int l = 0; l < a.L; ++l) {
     const uint16_t* xin = l == 0 ? static_cast<const uint16_t*>(a.x_in) : xb[(l - 1) & 1];
     uint16_t* xout = l == a.L - 1 ? static_cast<uint16_t*>(a.x_out) : xb[l & 1];
     lf::GemmParams g1{xin, static_cast<const uint16_t*>(a.w_qkv[l]), nullptr, nullptr, part, a.B, nq, a.H, 0, 0};
-    const lf::RopeParams rp{a.pos, q, kn, vn, a.B, a.Hq, a.Hkv, a.d, log2_base};
     if (lf::launch_gemm(g1, s, &rp) != hipSuccess) return LF_E_HIP;
     float* sc = (a.scores && a.scores[l]) ? a.scores[l] : ws_scores;
     int rc = lf::enqueue_decode_step(a.B, a.Hq, a.Hkv, a.d, a.S, a.scale, q, a.k_cache[l], a.v_cache[l],

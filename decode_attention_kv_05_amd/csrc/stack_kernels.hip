@@ -24,7 +24,8 @@
 // gemm_rope_epilogue_kernel takes the epilogue's place after the QKV
 // projection: it splits each sequence's qkv row into q [Hq][d], k [Hkv][d]
 // and v [Hkv][d] and rotates the q and k pairs (i, i + d/2) by
-// pos * base^(-2i/d) (angle in fp64, rotation in fp32).
+// pos * base^(-2i/d) (angle in fp64, rotation in fp32); rope_table_kernel
+// computes the angles' cosines and sines once per step.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -200,44 +201,73 @@ __global__ void gemm_epilogue_kernel(GemmParams p) {
   }
 }
 
-// The QKV projection's epilogue: sums the K-slice partials of columns
-// h d + i and h d + i + d/2 of head h (i < d/2), rounds them to bf16 (the
-// projection's output precision), rotates the pair by pos * base^(-2i/d)
-// for query and key heads (angle in fp64, rotation in fp32) and writes q, k
-// and v head by head.
-__global__ void gemm_rope_epilogue_kernel(GemmParams g, RopeParams p) {
+// The step's rotations: table[b][i] = (cos, sin) of pos[b] * base^(-2i/d),
+// angle in fp64, rounded to fp32.
+__global__ void rope_table_kernel(RopeParams p) {
   const int half = p.d / 2;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= p.B * half) return;
+  const int b = t / half, i = t - b * half;
+  const double ang = (double)p.pos[b] * exp2(-(2.0 * i / p.d) * p.log2_base);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  p.table[t] = make_float2((float)cs, (float)sn);
+}
+
+// The QKV projection's epilogue: sums the K-slice partials of columns
+// h d + i and h d + i + d/2 of head h (i < d/2), four values of i per
+// thread, rounds them to bf16 (the projection's output precision), rotates
+// the pairs of query and key heads by the step's table (in fp32) and writes
+// q, k and v head by head.
+__global__ void gemm_rope_epilogue_kernel(GemmParams g, RopeParams p) {
+  const int half = p.d / 2, quads = half / 4;
   const int heads = p.Hq + 2 * p.Hkv;
   const size_t plane = (size_t)g.M * g.N;
-  const size_t total = (size_t)p.B * heads * half;
+  const size_t total = (size_t)p.B * heads * quads;
   for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
        t += (size_t)gridDim.x * blockDim.x) {
-    const int i = (int)(t % half);
-    const size_t bh = t / half;
+    const int i = (int)(t % quads) * 4;
+    const size_t bh = t / quads;
     const int h = (int)(bh % heads);
     const int b = (int)(bh / heads);
     const float* src = g.part + (size_t)b * g.N + (size_t)h * p.d + i;
-    float s0 = src[0], s1 = src[half];
+    float4 s0 = *reinterpret_cast<const float4*>(src), s1 = *reinterpret_cast<const float4*>(src + half);
     for (int ks = 1; ks < g.ksplit; ++ks) {
-      s0 += src[ks * plane];
-      s1 += src[ks * plane + half];
+      const float4 x0 = *reinterpret_cast<const float4*>(src + ks * plane);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + ks * plane + half);
+      s0.x += x0.x;
+      s0.y += x0.y;
+      s0.z += x0.z;
+      s0.w += x0.w;
+      s1.x += x1.x;
+      s1.y += x1.y;
+      s1.z += x1.z;
+      s1.w += x1.w;
     }
-    const uint16_t x0 = f32_to_bf16_rne(s0), x1 = f32_to_bf16_rne(s1);
-    if (h >= p.Hq + p.Hkv) {
-      uint16_t* dst = p.v + ((size_t)b * p.Hkv + (h - p.Hq - p.Hkv)) * p.d;
-      dst[i] = x0;
-      dst[i + half] = x1;
-      continue;
+    uint16_t x0[4] = {f32_to_bf16_rne(s0.x), f32_to_bf16_rne(s0.y), f32_to_bf16_rne(s0.z), f32_to_bf16_rne(s0.w)};
+    uint16_t x1[4] = {f32_to_bf16_rne(s1.x), f32_to_bf16_rne(s1.y), f32_to_bf16_rne(s1.z), f32_to_bf16_rne(s1.w)};
+    uint16_t* dst;
+    if (h < p.Hq) {
+      dst = p.q + ((size_t)b * p.Hq + h) * p.d;
+    } else if (h < p.Hq + p.Hkv) {
+      dst = p.k + ((size_t)b * p.Hkv + (h - p.Hq)) * p.d;
+    } else {
+      dst = p.v + ((size_t)b * p.Hkv + (h - p.Hq - p.Hkv)) * p.d;
     }
-    const double ang = (double)p.pos[b] * exp2(-(2.0 * i / p.d) * p.log2_base);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    const float cf = (float)cs, sf = (float)sn;
-    const float a = bf16_to_f32(x0), bb = bf16_to_f32(x1);
-    uint16_t* dst = h < p.Hq ? p.q + ((size_t)b * p.Hq + h) * p.d
-                             : p.k + ((size_t)b * p.Hkv + (h - p.Hq)) * p.d;
-    dst[i] = f32_to_bf16_rne(a * cf - bb * sf);
-    dst[i + half] = f32_to_bf16_rne(bb * cf + a * sf);
+    if (h < p.Hq + p.Hkv) {
+      const float4* tab = reinterpret_cast<const float4*>(p.table + (size_t)b * half + i);
+      const float4 c01 = tab[0], c23 = tab[1];
+      const float cf[4] = {c01.x, c01.z, c23.x, c23.z}, sf[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = bf16_to_f32(x0[j]), bb = bf16_to_f32(x1[j]);
+        x0[j] = f32_to_bf16_rne(a * cf[j] - bb * sf[j]);
+        x1[j] = f32_to_bf16_rne(bb * cf[j] + a * sf[j]);
+      }
+    }
+    *reinterpret_cast<uint2*>(dst + i) = make_uint2(x0[0] | ((uint32_t)x0[1] << 16), x0[2] | ((uint32_t)x0[3] << 16));
+    *reinterpret_cast<uint2*>(dst + i + half) =
+        make_uint2(x1[0] | ((uint32_t)x1[1] << 16), x1[2] | ((uint32_t)x1[3] << 16));
   }
 }
 
@@ -297,7 +327,7 @@ hipError_t launch_gemm(const GemmParams& in, hipStream_t stream, const RopeParam
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (rope) {
-    const size_t total = (size_t)rope->B * (rope->Hq + 2 * rope->Hkv) * (rope->d / 2);
+    const size_t total = (size_t)rope->B * (rope->Hq + 2 * rope->Hkv) * (rope->d / 8);
     size_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(gemm_rope_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, prm, *rope);
@@ -306,6 +336,13 @@ hipError_t launch_gemm(const GemmParams& in, hipStream_t stream, const RopeParam
   size_t blocks = ((size_t)prm.M * prm.N / 4 + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(gemm_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const RopeParams& rope, hipStream_t stream) {
+  const int n = rope.B * (rope.d / 2);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, rope);
   return hipGetLastError();
 }
 

@@ -25,9 +25,12 @@ int gemm_ksplit(int N, int K);
 size_t gemm_partial_bytes(int M, int N, int K);
 
 // The QKV projection's output [B][(Hq + 2 Hkv) d] as q [B][Hq][d], k, v
-// [B][Hkv][d], with q and k rotated (RoPE at pos).
+// [B][Hkv][d], with q and k rotated (RoPE at pos): table[b][i] holds the
+// (cos, sin) of pos[b] * base^(-2i/d), i < d/2, filled by launch_rope_table
+// once per step (the positions hold for every layer of a step).
 struct RopeParams {
   const int32_t* pos;
+  float2* table;
   uint16_t* q;
   uint16_t* k;
   uint16_t* v;
@@ -37,6 +40,7 @@ struct RopeParams {
 
 // rope set: the epilogue writes q, k, v as RopeParams describes instead of C.
 hipError_t launch_gemm(const GemmParams& prm, hipStream_t stream, const RopeParams* rope = nullptr);
+hipError_t launch_rope_table(const RopeParams& rope, hipStream_t stream);
 hipError_t launch_advance_pos(int32_t* pos, int n, hipStream_t stream);
 
 }  // namespace lf

@@ -309,8 +309,9 @@ def test_stack_alias_errors():
 
 def test_stack_workspace_size():
     """The decode workspace first, then q, k, v, O, two activation buffers, a
-    scores buffer and the projections' split-K partials (fp32, the larger of
-    the two projections), each rounded up to 256 bytes."""
+    scores buffer, the step's RoPE table (B x d/2 (cos, sin) pairs) and the
+    projections' split-K partials (fp32, the larger of the two projections),
+    each rounded up to 256 bytes."""
     up = lambda n: -(-n // 256) * 256
 
     def ksplit(N, K):  # the projection's K slices: whole 256-deep pieces, at most 8 per slice,
@@ -325,7 +326,7 @@ def test_stack_workspace_size():
         for ns in (1, 3):
             dec = lf.lf_workspace_size(B, Hq, Hkv, d, S, ns)
             want = up(dec) + up(B * Hq * d * 2) + 2 * up(B * Hkv * d * 2) \
-                + up(B * Hq * d * 2) + 2 * up(B * H * 2) + up(B * Hkv * S * 4) + up(part)
+                + up(B * Hq * d * 2) + 2 * up(B * H * 2) + up(B * Hkv * S * 4) + up(B * (d // 2) * 8) + up(part)
             assert lf.lf_stack_workspace_size(L, B, H, Hq, Hkv, d, S, ns) == want
     assert ksplit(6144, 4096) == 4 and ksplit(4096, 4096) == 8
     assert ksplit(7168, 5120) == 4 and ksplit(5120, 5120) == 5 and ksplit(256, 2304) == 9
