@@ -250,8 +250,9 @@ constexpr float kInf = __builtin_huge_valf();
 // Stagger of the streaming order in the split and team modes: each wave
 // starts at batch (workgroup index * kRotate) mod (its batch count).
 // Splits of a power-of-two number of rows otherwise stream in lockstep from
-// addresses a power of two apart (long_reasoning: 269.8 -> 248.6 us/step);
-// the single-split kernel measured no better staggered (ragged 3% slower),
+// addresses a power of two apart (batch 16, 64/8 heads, 16384 slots in 4
+// splits: 269.8 -> 248.6 us/step); the single-split kernel measured no
+// better staggered (the ragged batch of 256 sequences 3% slower),
 // so it streams in order.
 constexpr int kRotate = 5;
 
@@ -1030,8 +1031,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     // pairs from the work-item counter (tickets gridDim.x, gridDim.x + 1, ...)
     // until none is left, so a compute unit that streams faster takes more
     // pairs.  (The dispatcher deals workgroups to the 8 XCDs in turn, and the
-    // XCDs stream at different rates: with one workgroup per pair, qwen3_8b's
-    // first pairs took 105 us on the fastest XCDs and 140 us on the slowest,
+    // XCDs stream at different rates: with one workgroup per pair, the first
+    // pairs of batch 128 x 8 KV heads x 3200 slots took 105 us on the fastest
+    // XCDs and 140 us on the slowest,
     // and the ragged batch's long sequences ended the step on slow XCDs.  The
     // first pair goes by block index because 512 workgroups starting on one
     // counter at once spread their starts over 5 us.)
