@@ -94,6 +94,28 @@ def measured_traffic(tag):
     return rec.get("bytes_per_launch")
 
 
+def measured_lds(name):
+    """LDS bank conflicts of the decode kernel on this workload from the
+    committed rocprofv3 counter run (profiles/longflow_decode_<name>_counters.txt),
+    if it was taken on the current decode sources; else None."""
+    path = os.path.join(PROFILES, f"longflow_decode_{name}_counters.txt")
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    from decode_attention_kv_05_amd.build import source_hash
+    if f"kernel sources (decode): {source_hash('decode')}" not in text:
+        return None
+    rec = {"source": os.path.relpath(path, os.path.dirname(os.path.abspath(__file__)))}
+    for line in text.splitlines():
+        if line.startswith("SQ_LDS_BANK_CONFLICT"):
+            rec["bank_conflict_cycles_per_dispatch"] = float(line.split()[1])
+        elif line.startswith("LDS bank-conflict cycles / LDS active cycles"):
+            rec["bank_conflict_frac_of_lds_active"] = float(line.split()[-1])
+    return rec if len(rec) == 3 else None
+
+
 def host_cores():
     """Threads the CPU baseline may use: the process's CPU share, at most 16
     (the host share of one GPU)."""
@@ -131,20 +153,68 @@ def _per_sequence(fn, nb, workers):
         return list(ex.map(fn, range(nb)))
 
 
-def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
+def cpu_baseline_sequences(wl, max_pairs):
+    """Sequences the decode CPU baseline runs: the first ceil(max_pairs / Hkv)."""
+    return max(1, min(wl.B, -(-max_pairs // wl.Hkv)))
+
+
+def parity_verdict(wl, mask, gpu, ref):
+    """The GPU's first step against the oracle's on the sampled sequences, by
+    the acceptance rule of the parity tests: O within 1e-2 + 1e-2 |O_ref|,
+    valid scores within 1e-3 relative and masked ones +inf, the evicted slot
+    exact or inside a near-tie band of 1e-4 relative."""
+    o_ref, s_ref, e_ref = ref
+    G = wl.Hq // wl.Hkv
+    n = len(e_ref)
+    passed = exact = 0
+    o_err = s_rel = 0.0
+    for b in range(n):
+        valid = mask[b] != 0
+        for j in range(wl.Hkv):
+            og, orf = gpu["out"][b, j * G:(j + 1) * G], o_ref[b, j * G:(j + 1) * G]
+            err = np.abs(og - orf)
+            ok = bool(np.all(err <= 1e-2 + 1e-2 * np.abs(orf)))
+            o_err = max(o_err, float(err.max()))
+            sg, sr = gpu["scores"][b, j], s_ref[b, j]
+            ok &= bool(np.all(np.isposinf(sg[~valid])))
+            if valid.any():
+                rel = np.abs(sg[valid] - sr[valid]) / np.maximum(sr[valid], 1e-300)
+                s_rel = max(s_rel, float(rel.max()))
+                ok &= bool(np.all(rel <= 1e-3))
+            eg, er = int(gpu["evict"][b, j]), int(e_ref[b, j])
+            if eg == er:
+                exact += 1
+            elif er >= 0 and 0 <= eg < wl.S and valid[eg]:
+                vals = np.sort(sr[valid])
+                s1, s2 = vals[0], (vals[1] if vals.size > 1 else np.inf)
+                ok &= bool((sr[eg] == 0) if s1 == 0 else ((s2 - s1) / s1 < 1e-4 and sr[eg] <= s1 * (1 + 1e-4)))
+            else:
+                ok = False
+            passed += ok
+    pairs = n * wl.Hkv
+    return {"verdict": "pass" if passed == pairs else "fail", "pairs": pairs, "pairs_passed": passed,
+            "step": 0, "evict_exact": exact, "o_max_abs_err": o_err, "score_max_rel_err": s_rel,
+            "rule": "O 1e-2 + 1e-2|ref|; scores 1e-3 rel, masked +inf; evict exact or 1e-4 near-tie"}
+
+
+def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0, gpu_step0=None):
     """The fp64 oracle on the host cores, on a bounded sample of the same
     workload: up to `max_pairs` (sequence, KV head) pairs per step, one
     sequence per task on a thread pool, over consecutive steps until
-    `min_seconds` of wall time, scaled by valid K/V bytes to whole steps."""
+    `min_seconds` of wall time, scaled by valid K/V bytes to whole steps.
+    With gpu_step0 (the GPU's outputs of step 0 on the same sequences), the
+    oracle's first step also gives a parity verdict (returned under
+    "parity")."""
     from decode_attention_kv_05_amd import workloads as W
     from oracle import decode_step
 
-    nb = max(1, min(wl.B, -(-max_pairs // wl.Hkv)))
+    nb = cpu_baseline_sequences(wl, max_pairs)
     batch = list(range(nb))
     k, v, m = W.initial_cache(wl, batch)
     prev = W.first_prev_slot(wl, batch)
     cores = host_cores()
     steps, busy = 0, 0.0
+    parity = None
     while busy < min_seconds and steps < wl.steps:
         q, nk, nv = W.step_inputs(wl, steps, batch)
         t0 = time.perf_counter()
@@ -152,6 +222,8 @@ def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
                                                   nv[b:b + 1], prev[b:b + 1], wl.scale), nb, cores)
         busy += time.perf_counter() - t0
         prev = np.concatenate([r[2] for r in res])
+        if steps == 0 and gpu_step0 is not None:
+            parity = parity_verdict(wl, m, gpu_step0, tuple(np.concatenate([r[i] for r in res]) for i in range(3)))
         steps += 1
     frac = valid_slots(m) / max(1, valid_slots(mask))
     s_per_step = busy / steps / frac
@@ -168,6 +240,7 @@ def cpu_baseline(wl, mask, max_pairs, min_seconds=10.0):
         "s_per_step": round(s_per_step, 3),
         "cpu_model": model,
         "blas": blas,
+        **({"parity": parity} if parity is not None else {}),
     }
 
 
@@ -491,6 +564,18 @@ def main():
             dm.copy_(dm0)
             slots[t % 2].fill_(fill_from if fill_from < wl.S else -1)
 
+    # The first step once more before the timing, for the parity verdict of
+    # the CPU baseline leg: it writes no cache row (prev_slot -1) and only
+    # sets slots[1], so the timed run starts from the same state.
+    gpu_step0 = None
+    if args.mode == "decode" and not args.no_cpu_baseline:
+        nb = cpu_baseline_sequences(wl, args.cpu_pairs)
+        step(0)
+        torch.cuda.synchronize(dev)
+        gpu_step0 = {"out": out[:nb].float().cpu().numpy().astype(np.float64),
+                     "scores": scores[:nb].cpu().numpy().astype(np.float64),
+                     "evict": slots[1][:nb].cpu().numpy()}
+
     reps, per_launch, wall, warm = timed(step, K, Wm, stream, dev, reset, args.warmup_seconds)
     ms_per_step = float(np.median(reps))
     status = lf.lf_read_device_status(ws)
@@ -551,6 +636,8 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     result["hbm_probe"] = hbm_probes(dev, dk, dv)
+    if args.mode != "cadence":
+        result["lds"] = measured_lds(wl.name if args.mode == "decode" else f"fill_{wl.name}")
     if args.mode == "fill":
         result["config"].update({"mode": "fill", "start_valid_slots": fill_from})
     if args.mode == "cadence":
@@ -563,7 +650,10 @@ def main():
         if args.mode == "fill":
             result["cpu_baseline"] = cpu_baseline_fill(wl, args.cpu_pairs, fill_from)
         else:
-            result["cpu_baseline"] = cpu_baseline(wl, mask, args.cpu_pairs)
+            result["cpu_baseline"] = cpu_baseline(wl, mask, args.cpu_pairs, gpu_step0=gpu_step0)
+            parity = result["cpu_baseline"].pop("parity", None)
+            if parity is not None:
+                result["parity"] = parity
         log(f"cpu baseline took {time.time() - t0:.1f} s")
     print(json.dumps(result), flush=True)
 
