@@ -32,13 +32,14 @@ struct DecodeParams {
   uint64_t* xfin;         // team: [pairs][nsplit][3] published minimum (high, low word), lowest free slot
   uint64_t* xo;           // team: [pairs][nsplit][GP][d] published O accumulators
   uint32_t* xcnt;         // team: [pairs] splits finished
-  uint32_t* xticket;      // team: [kTicketRanges] work items handed out per range
+  uint32_t* xticket;      // team: [kTicketRanges] work items handed out per range (ticket_ranges used)
   uint32_t* lens;         // one split, longest-first schedule: [pairs] one past each pair's last
                           // valid slot; null without the schedule
   uint32_t* order;        // [2][kOrderMaxPairs] pair orders (one read, the other rebuilt)
   int pairs;              // B * Hkv
   int Hq, Hkv, G, S, nsplit, split_len;
   int fill;               // 1: fill step (next slot = lowest free slot while any)
+  int ticket_ranges;      // team: ticket ranges in use, 1 .. kTicketRanges
   float qscale;           // logit scale times log2(e)
 };
 

@@ -29,12 +29,16 @@ constexpr int kMaxSplits = 1024;      // slot splits per (sequence, KV head)
 // (max, sum) words of all the others, so the exchange grows with the square
 // of the count; beyond this the combine path finishes the step.
 constexpr int kMaxTeamSplits = 64;
-// Ticket counters of the team path; range r holds pairs
-// [ticket_range_first_pair(pairs, r), ticket_range_first_pair(pairs, r + 1)).
+// Ticket counters of the team path: a launch uses `ranges` of them (1 to
+// kTicketRanges), range r holding pairs [ticket_range_first_pair(pairs, r,
+// ranges), ticket_range_first_pair(pairs, r + 1, ranges)).
 constexpr int kTicketRanges = 8;
-LF_HD inline int ticket_range_first_pair(int pairs, int r) {
-  return (int)((long long)pairs * r / kTicketRanges);
+LF_HD inline int ticket_range_first_pair(int pairs, int r, int ranges) {
+  return (int)((long long)pairs * r / ranges);
 }
+// XCDs of an MI355X: a launch's workgroups are dealt to them in turn, in
+// block order, and each waits for room on its own XCD.
+constexpr int kXcds = 8;
 // LDS bytes a workgroup may spend on the logits of its slot range.
 constexpr size_t kLogitLdsBudget = (size_t)136 * 1024;
 

@@ -218,16 +218,27 @@ int validate_step(int B, int Hq, int Hkv, int d, int S, float scale, const void*
 
 namespace lf {
 
-// Whether the device holds more team-kernel workgroups at once than can
-// ever be waiting, which is all the team path needs: its workgroups take
-// (pair, split) tickets in the order they start, so in each ticket range
-// every team but the one holding the newest ticket is already running.
-static bool device_holds_teams(int d, int gp, int nw, size_t lds, int nsplit_eff) {
-  if (nsplit_eff < 2 || nsplit_eff > lf::kMaxTeamSplits) return false;
+// Ticket ranges for a team launch, or 0 when the team path cannot be taken.
+// Its workgroups take (pair, split) tickets in the order they start, so in
+// each range every team but the one holding the newest ticket is already
+// running, and at most ranges * (nsplit - 1) workgroups ever wait for
+// teammates that have not started.  Workgroups are dealt to the XCDs in
+// turn and dispatched in block order, each waiting for room on its own XCD,
+// and the waiting ones may all sit on one XCD; the next workgroup bound for
+// it then starts only if that XCD also holds a workgroup that is not
+// waiting.  So one XCD must hold more workgroups at once than can ever be
+// waiting; the most ranges (of 8, 4, 2, 1) for which it does are used.
+// (Counting the whole device instead let 64-split steps on 256 CUs stall
+// until the waits' deadline now and then.)
+static int team_ticket_ranges(int d, int gp, int nw, size_t lds, int nsplit_eff) {
+  if (nsplit_eff < 2 || nsplit_eff > lf::kMaxTeamSplits) return 0;
   int per_cu = 0, cus = 0;
-  if (lf_device_num_cus(&cus) != LF_OK) return false;
-  if (lf::decode_blocks_per_cu(true, d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return false;
-  return (int64_t)per_cu * cus > (int64_t)lf::kTicketRanges * (nsplit_eff - 1);
+  if (lf_device_num_cus(&cus) != LF_OK) return 0;
+  if (lf::decode_blocks_per_cu(true, d, gp, nw, lds, &per_cu) != hipSuccess || per_cu < 1) return 0;
+  const int64_t per_xcd = (int64_t)per_cu * (cus >= lf::kXcds ? cus / lf::kXcds : cus);
+  for (int r = lf::kTicketRanges; r >= 1; r /= 2)
+    if (per_xcd > (int64_t)r * (nsplit_eff - 1)) return r;
+  return 0;
 }
 
 // Enqueue one step after validation: the decode kernel, and for several
@@ -291,11 +302,13 @@ int enqueue_decode_step(int B, int Hq, int Hkv, int d, int S, float scale, const
     const lf::TeamLayout tl = lf::team_layout(wl, B, Hkv, d, gp, eff);
     const int nw_team = lf::decode_waves(gp, len, true);
     const size_t lds_team = lf::lds_layout(d, gp, len, nw_team, true).total;
-    team_grid = lds_team <= lf::kMaxLdsBytes && device_holds_teams(d, gp, nw_team, lds_team, eff) ? nblocks : 0;
+    const int ranges = lds_team <= lf::kMaxLdsBytes ? team_ticket_ranges(d, gp, nw_team, lds_team, eff) : 0;
+    team_grid = ranges > 0 ? nblocks : 0;
     if (team_grid == 0 && split_path == LF_SPLIT_TEAM) return LF_E_NSPLIT;
     if (team_grid > 0) {
       nw = nw_team;
       lds = lds_team;
+      prm.ticket_ranges = ranges;
     }
     prm.xstat = reinterpret_cast<uint64_t*>(ws + tl.xstat);
     prm.xfin = reinterpret_cast<uint64_t*>(ws + tl.xfin);
@@ -504,7 +517,7 @@ extern "C" int longflow_decode_noalloc(int B, int Hq, int Hkv, int d, int S, flo
   if (eff > 1) {
     const int nw = lf::decode_waves(gp, len, true);
     const size_t lds = lf::lds_layout(d, gp, len, nw, true).total;
-    team_only = lds <= lf::kMaxLdsBytes && lf::device_holds_teams(d, gp, nw, lds, eff);
+    team_only = lds <= lf::kMaxLdsBytes && lf::team_ticket_ranges(d, gp, nw, lds, eff) > 0;
     need = team_only ? lf::team_workspace_bytes(B, Hkv, d, gp, eff)
                      : lf::workspace_layout(B, Hkv, d, S, gp, eff).total;
   }

@@ -1102,25 +1102,27 @@ __global__ __launch_bounds__(NW * 64, waves_per_eu(GP)) void longflow_decode_ker
     }
   } else if constexpr (MODE == kModeTeam) {
     // Work items go out by tickets in the order workgroups start, not by
-    // block index.  The pairs form kTicketRanges ranges of whole teams, each
-    // with its own counter (left at zero by the previous launch); a workgroup
-    // claims from range (block index mod kTicketRanges) first and from the
+    // block index.  The pairs form p.ticket_ranges ranges of whole teams,
+    // each with its own counter (left at zero by the previous launch); a
+    // workgroup claims from range (block index mod ranges) first and from the
     // next ranges once that one is used up.  There are as many workgroups as
     // items, so every claim succeeds.  Within a range tickets go out in start
     // order, so every team of a range except the one holding its newest
-    // ticket has all its members running: at most kTicketRanges *
-    // (nsplit - 1) workgroups ever wait for members that have not started,
-    // and only until some running workgroup ends.  The launch completes
-    // whenever the device holds more than that at once, whatever the
-    // dispatch order.  (One counter for all made 256 workgroups queue on one
-    // atomic as a wave of them started: 3-4% slower.)
+    // ticket has all its members running: at most ranges * (nsplit - 1)
+    // workgroups ever wait for members that have not started, and only until
+    // some running workgroup ends.  The host picks the number of ranges so
+    // that one XCD holds more workgroups at once than that, since a
+    // workgroup waits for room on the XCD it is dealt to.  (One counter for
+    // all made 256 workgroups queue on one atomic as a wave of them started:
+    // 3-4% slower, so the most ranges that fit are used.)
     const int nsplit = p.nsplit;
+    const int ranges = p.ticket_ranges;
     if (threadIdx.x == 0) {
       int claimed = -1;
-      for (int k = 0; k < kTicketRanges && claimed < 0; ++k) {
-        const int r = (int)((blockIdx.x + k) % kTicketRanges);
-        const int lo = ticket_range_first_pair(p.pairs, r) * nsplit;
-        const int hi = ticket_range_first_pair(p.pairs, r + 1) * nsplit;
+      for (int k = 0; k < ranges && claimed < 0; ++k) {
+        const int r = (int)((blockIdx.x + k) % ranges);
+        const int lo = ticket_range_first_pair(p.pairs, r, ranges) * nsplit;
+        const int hi = ticket_range_first_pair(p.pairs, r + 1, ranges) * nsplit;
         if (lo == hi) continue;
         const unsigned t = atomicAdd(p.xticket + r, 1u);
         if (t < (unsigned)(hi - lo)) claimed = lo + (int)t;

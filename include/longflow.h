@@ -128,9 +128,11 @@ typedef enum lf_status {
                               streamed its whole slot range);
                               the last split of a pair to finish writes O and
                               the evicted slot.  Workgroups take (pair, split)
-                              tickets in the order they start, so the step
-                              completes whenever the device holds more than
-                              8 * (nsplit - 1) of them at once */
+                              tickets in the order they start, from R ticket
+                              ranges, so the step completes whenever one XCD
+                              holds more than R * (nsplit - 1) of them at once;
+                              the library picks R (8, 4, 2 or 1) from the
+                              occupancy query, else takes the combine path */
 
 /* ABI version (LF_ABI_VERSION). */
 int lf_version(void);

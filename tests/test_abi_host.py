@@ -383,9 +383,11 @@ int main() {
       ++bad;
   }
   for (int pairs = 1; pairs < 3000; pairs += 7) {
-    if (lf::ticket_range_first_pair(pairs, 0) != 0 || lf::ticket_range_first_pair(pairs, lf::kTicketRanges) != pairs) ++bad;
-    for (int r = 0; r < lf::kTicketRanges; ++r)
-      if (lf::ticket_range_first_pair(pairs, r + 1) < lf::ticket_range_first_pair(pairs, r)) ++bad;
+    for (int rg = 1; rg <= lf::kTicketRanges; rg *= 2) {
+      if (lf::ticket_range_first_pair(pairs, 0, rg) != 0 || lf::ticket_range_first_pair(pairs, rg, rg) != pairs) ++bad;
+      for (int r = 0; r < rg; ++r)
+        if (lf::ticket_range_first_pair(pairs, r + 1, rg) < lf::ticket_range_first_pair(pairs, r, rg)) ++bad;
+    }
   }
   printf("%d %d\n", cases, bad);
   return 0;
