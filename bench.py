@@ -15,7 +15,7 @@ device.  After at least W warm-up steps and at least one second of them
 pair of events, five times over; the median of the five is the reported
 time per step.  K further steps, each between its own pair of events, give
 per-launch durations as a second figure, and plain device copy and read
-probes on the same GPU give the box's practical HBM rates.  Prints one JSON
+probes on the same GPU give its practical HBM rates.  Prints one JSON
 line.
 
 Other modes measure the cache-lifecycle entry points on the same shape:
@@ -367,7 +367,7 @@ def timed(step, K, Wm, stream, dev, reset=None, warmup_s=WARMUP_MIN_S):
 
 
 def hbm_probes(dev, k_cache=None, v_cache=None, reps=5):
-    """The GPU's practical HBM read rates on this machine, measured in the same
+    """The GPU's practical HBM read rates, measured in the same
     run by plain read kernels (libhbm_probe.so, not the library): the whole
     grid reading in address order, and the decode's own pattern without its
     arithmetic (K then V of each (sequence, KV head) pair, one workgroup per
